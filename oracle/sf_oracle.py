@@ -1,0 +1,345 @@
+"""Oracle: a plain CPU restatement of the Summaryformer per-block memory.
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its Python binding) never imports, calls or links it,
+and this module imports nothing from the product.  The two share only the
+seeded input generators of ``sf_inputs``.
+
+Everything is numpy on the host.  Floating-point arithmetic is fp64.  Stored
+buffer contents keep the bytes the caller handed in (float32 values, or the
+uint16 bit patterns of bfloat16), so byte-exact comparison is direct.
+
+Source.  The method is described on one web page, the model card titled
+"GTA world model: weights and inference code" (Summaryformer).  Citations in
+this file name its parts:
+
+  [caption]  the caption at the top of the page: the start image and the
+             newest three frames kept whole, 22 older frames kept as 96
+             summary tokens each; 6,528 keys instead of 26,208.
+  [record]   section "A frame is a record": record(t) is the H*W raw tokens
+             followed by the X summary tokens.
+  [attends]  section "What a frame attends to": the four-item list.
+  [buffer]   section "One buffer, no mask": the Z0 | RAW | SUM layout, the
+             eviction paragraph, the figure "The buffer one frame apart",
+             the parameter table and the dense, unmasked read.
+  [sampling] section "The rest of the model", the "Sampling" item: a clean
+             pass rewrites the frame's entry in memory.
+
+Readings where the page leaves a step open (each is listed in the design doc):
+  * Frame 0 is the start image and lives in Z0; generated frames are t >= 1.
+  * RAW slot of frame t is t mod (Y+1); SUM slot of frame f is f mod (W-Y).
+  * In one step, the eviction runs before the new record is written.
+  * Softmax scale defaults to 1/sqrt(head_dim).
+  * Empty slots hold zeros and are never read.
+
+Pin status.  Every function below is pinned by tests/test_oracle_pins.py
+against facts the page fixes (the figure's worked example, the caption's key
+counts, brute-force equality with the attention-set rule, closed forms of
+softmax attention, torch's float64 SDPA over gathered rows).  No function
+here is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Geometry of one buffer
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Geometry:
+    """Shape of the memory of one session ([record], [buffer] parameter table).
+
+    hw: raw tokens per frame (one per latent grid cell); x: summary tokens per
+    frame; y: frames kept whole before the current one; w: memory window in
+    frames; plus heads, head_dim, blocks and the storage type of Q/K/V.
+    """
+
+    hw: int
+    x: int
+    y: int
+    w: int
+    n_heads: int
+    head_dim: int
+    n_blocks: int = 1
+    dtype: str = "bf16"
+
+    @property
+    def r(self) -> int:
+        """Rows of one record: H*W raw rows then X summary rows ([record])."""
+        return self.hw + self.x
+
+    @property
+    def n_raw(self) -> int:
+        """RAW slots: the current frame and the Y before it ([buffer])."""
+        return self.y + 1
+
+    @property
+    def n_sum(self) -> int:
+        """SUM slots: one per older frame inside the window ([buffer])."""
+        return self.w - self.y
+
+    @property
+    def capacity(self) -> int:
+        """Rows of the whole buffer: Z0, then Y+1 records, then W-Y summaries."""
+        return self.r * (self.y + 2) + self.n_sum * self.x
+
+    def z0_rows(self):
+        return 0, self.r
+
+    def raw_rows(self, s: int):
+        return self.r * (1 + s), self.r * (2 + s)
+
+    def sum_rows(self, u: int):
+        base = self.r * (self.y + 2)
+        return base + u * self.x, base + (u + 1) * self.x
+
+    @classmethod
+    def from_workload(cls, wl: dict) -> "Geometry":
+        return cls(wl["hw"], wl["x"], wl["y"], wl["w"], wl["n_heads"],
+                   wl["head_dim"], wl["n_blocks"], wl["dtype"])
+
+
+# --------------------------------------------------------------------------
+# Numbers
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns: they are the top half of a float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def stored_to_f64(a: np.ndarray) -> np.ndarray:
+    """fp64 value of stored Q/K/V bytes (uint16 = bfloat16 bits, else a float type)."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+def default_scale(head_dim: int) -> float:
+    """Softmax scale when the caller gives none: 1/sqrt(head_dim)."""
+    return 1.0 / np.sqrt(float(head_dim))
+
+
+def attention_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Exact softmax attention, every query row against every key row, per head.
+
+    q: [n][H][d], k and v: [m][H][d], all fp64.  Returns [n][H][d] fp64:
+    O[i,h] = sum_j softmax_j(scale * <q[i,h], k[j,h]>) v[j,h].  No mask and
+    no causal order ([buffer]: the read is one dense, unmasked attention).
+    Subtracting the row maximum before exp leaves the exact value unchanged.
+    """
+    n, n_heads, _ = q.shape
+    out = np.empty((n, n_heads, v.shape[2]), dtype=np.float64)
+    for h in range(n_heads):
+        s = (q[:, h, :] @ k[:, h, :].T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        out[:, h, :] = (p @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+# --------------------------------------------------------------------------
+# The attention-set rule, stated on frame ids (no buffer)
+# --------------------------------------------------------------------------
+def frame_visibility(g: Geometry, t: int, f: int) -> str:
+    """What frame t's tokens see of frame f ([attends]): 'whole', 'summary' or 'none'.
+
+    Frame 0 (the start image) is always seen whole.  Frame t itself and the Y
+    frames before it are seen whole.  Older frames inside the window of W
+    frames before t are seen through their X summary rows only.  Generated
+    frames are numbered from 1.
+    """
+    if f == 0:
+        return "whole"
+    if f < 1 or f > t:
+        return "none"
+    if f >= t - g.y:
+        return "whole"
+    if f >= t - g.w:
+        return "summary"
+    return "none"
+
+
+def history_mask(g: Geometry, t: int) -> np.ndarray:
+    """Boolean mask over the concatenated records 0..t: may frame t see this row?"""
+    rows = np.arange(g.r)
+    parts = []
+    for f in range(t + 1):
+        vis = frame_visibility(g, t, f)
+        if vis == "whole":
+            parts.append(np.ones(g.r, dtype=bool))
+        elif vis == "summary":
+            parts.append(rows >= g.hw)
+        else:
+            parts.append(np.zeros(g.r, dtype=bool))
+    return np.concatenate(parts)
+
+
+def history_attention(g: Geometry, t: int, q: np.ndarray, hist_k, hist_v, scale: float) -> np.ndarray:
+    """Brute-force twin: masked attention over the full history of records.
+
+    hist_k / hist_v: sequences of fp64 [R][H][d] records for frames 0..t (the
+    last write of each).  The mask is ``history_mask``; masked scores are
+    dropped from the softmax.  Equal to the buffer read when the buffer keeps
+    exactly what [attends] lists.
+    """
+    keys = np.concatenate([np.asarray(hist_k[f]) for f in range(t + 1)], axis=0)
+    vals = np.concatenate([np.asarray(hist_v[f]) for f in range(t + 1)], axis=0)
+    m = history_mask(g, t)
+    return attention_f64(q, keys[m], vals[m], scale)
+
+
+def key_count(g: Geometry, t: int) -> int:
+    """Readable rows at frame t, counted from the attention-set rule ([attends]).
+
+    Z0's record, the whole records of frames max(1, t-Y)..t, and X summary
+    rows for each frame max(1, t-W)..t-Y-1.
+    """
+    if t == 0:
+        return g.r
+    whole = t - max(1, t - g.y) + 1
+    summarised = max(0, (t - g.y - 1) - max(1, t - g.w) + 1)
+    return g.r + whole * g.r + summarised * g.x
+
+
+# --------------------------------------------------------------------------
+# The buffer replay
+# --------------------------------------------------------------------------
+class MemoryReplay:
+    """One session's per-block K/V buffers, replayed step by step on the host.
+
+    The layout follows [buffer]: rows [0, R) hold Z0 (record 0, never evicted);
+    RAW slot s holds rows [R(1+s), R(2+s)); SUM slot u holds rows
+    [R(Y+2) + uX, R(Y+2) + (u+1)X).  K and V of a block are each
+    [capacity][H][d] in storage bytes.  ``blocks`` limits the replay to a
+    subset of blocks (blocks are independent); by default all are kept.
+    """
+
+    def __init__(self, g: Geometry, blocks=None):
+        self.g = g
+        self.blocks = list(range(g.n_blocks)) if blocks is None else list(blocks)
+        self.index = {b: i for i, b in enumerate(self.blocks)}
+        store = np.uint16 if g.dtype == "bf16" else np.float32
+        shape = (len(self.blocks), g.capacity, g.n_heads, g.head_dim)
+        self.k = np.zeros(shape, dtype=store)
+        self.v = np.zeros(shape, dtype=store)
+        self.raw_frame = [-1] * g.n_raw    # frame id held by each RAW slot
+        self.sum_frame = [-1] * g.n_sum    # frame id whose summary each SUM slot holds
+        self.t = -1
+
+    # -- slot map ([buffer] figure "The buffer one frame apart") -----------
+    def raw_slot(self, t: int) -> int:
+        return t % self.g.n_raw
+
+    def sum_slot(self, f: int) -> int:
+        return f % self.g.n_sum
+
+    # -- eviction ([buffer], eviction paragraph) ---------------------------
+    def evict(self, t: int):
+        """Before frame t is written: move the summary of the frame leaving RAW into SUM.
+
+        The frame leaving is the one in RAW slot t mod (Y+1).  Only its X
+        summary rows (record rows [HW, R)) are copied, K and V, in every block;
+        its raw rows stay where they are, to be overwritten by frame t.  Frame
+        0 is never in RAW, so nothing moves while that slot is still empty.
+        Returns (raw slot, sum slot, frame) or None.
+        """
+        g = self.g
+        if t <= g.y:
+            return None
+        s = self.raw_slot(t)
+        f = self.raw_frame[s]
+        if f < 1:
+            return None
+        u = self.sum_slot(f)
+        src0 = g.raw_rows(s)[0] + g.hw
+        src1 = g.raw_rows(s)[1]
+        dst0, dst1 = g.sum_rows(u)
+        self.k[:, dst0:dst1] = self.k[:, src0:src1]
+        self.v[:, dst0:dst1] = self.v[:, src0:src1]
+        self.sum_frame[u] = f
+        return s, u, f
+
+    # -- record write ([buffer]; rewrite: [sampling]) ----------------------
+    def write(self, block: int, t: int, k: np.ndarray, v: np.ndarray):
+        """Store record(t)'s K and V ([R][H][d] storage bytes) in its rows of one block.
+
+        Frame 0 goes to Z0; frame t >= 1 to RAW slot t mod (Y+1).  Writing the
+        same t again overwrites (the clean pass rewrites the frame's entry).
+        """
+        g = self.g
+        if t == 0:
+            lo, hi = g.z0_rows()
+        else:
+            s = self.raw_slot(t)
+            lo, hi = g.raw_rows(s)
+            self.raw_frame[s] = t
+        i = self.index[block]
+        self.k[i, lo:hi] = np.asarray(k).reshape(g.r, g.n_heads, g.head_dim)
+        self.v[i, lo:hi] = np.asarray(v).reshape(g.r, g.n_heads, g.head_dim)
+        self.t = t
+
+    def step(self, t: int, records: dict):
+        """Frame t: eviction (if due) then the write of every block in ``records``."""
+        ev = self.evict(t) if t >= 1 else None
+        for b, (k, v) in records.items():
+            self.write(b, t, k, v)
+        return ev
+
+    # -- the dense read ([buffer]: what is in the buffer is what is seen) --
+    def readable_segments(self):
+        """Filled rows, ascending, as (begin, length) segments of contiguous rows."""
+        g = self.g
+        if self.t < 0:
+            return []
+        ranges = [g.z0_rows()]
+        ranges += [g.raw_rows(s) for s in range(g.n_raw) if self.raw_frame[s] >= 1]
+        ranges += [g.sum_rows(u) for u in range(g.n_sum) if self.sum_frame[u] >= 1]
+        ranges.sort()
+        segs = []
+        for lo, hi in ranges:
+            if segs and segs[-1][0] + segs[-1][1] == lo:
+                segs[-1] = (segs[-1][0], segs[-1][1] + hi - lo)
+            else:
+                segs.append((lo, hi - lo))
+        return segs
+
+    def readable_rows(self) -> np.ndarray:
+        segs = self.readable_segments()
+        if not segs:
+            return np.zeros(0, dtype=np.int64)
+        return np.concatenate([np.arange(b, b + n) for b, n in segs])
+
+    def n_keys(self) -> int:
+        return sum(n for _, n in self.readable_segments())
+
+    def gathered(self, block: int):
+        """fp64 K and V of the readable rows of one block, ascending row order."""
+        rows = self.readable_rows()
+        i = self.index[block]
+        return stored_to_f64(self.k[i, rows]), stored_to_f64(self.v[i, rows])
+
+    def attend(self, block: int, q: np.ndarray, scale=None, rows=None) -> np.ndarray:
+        """Frame t's record attends to every readable row of one block, fp64.
+
+        q: [R][H][d] storage bytes (or fp64).  ``rows`` optionally restricts the
+        query rows computed (for sampled checks at large sizes).
+        """
+        g = self.g
+        if scale is None or scale <= 0:
+            scale = default_scale(g.head_dim)
+        qf = stored_to_f64(np.asarray(q).reshape(-1, g.n_heads, g.head_dim))
+        if rows is not None:
+            qf = qf[np.asarray(rows)]
+        kf, vf = self.gathered(block)
+        return attention_f64(qf, kf, vf, scale)
+
+    # -- bytes --------------------------------------------------------------
+    def block_bytes(self, block: int) -> bytes:
+        """Canonical bytes of one block: K [capacity][H][d] then V."""
+        i = self.index[block]
+        return self.k[i].tobytes() + self.v[i].tobytes()
