@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of the Summaryformer per-block memory on one MI355X.
+
+Workload: the served rollout in steady state -- 28 blocks, 16 heads of 64,
+24x42 = 1008 raw tokens + 96 summary tokens per record, Y = 2, W = 24, so
+every attention reads 6,528 keys (model card "GTA world model: weights and
+inference code": the caption at the top and section "One buffer, no mask").
+One step is one frame through all 28 blocks: the all-block eviction, then per
+block the record write and the dense attention read, through the C-ABI.
+Inputs are seeded N(0,1) bf16 tensors already resident in HBM; the session is
+prefilled through frames 0..25 (untimed) and timed frames cycle through 8
+seeded frames' inputs while frame ids, slots and evictions advance normally.
+
+Prints one JSON line.  Kernel durations come from HIP events recorded on the
+stream the library launches on, around each call inside the timed region.
+The cpu_baseline leg times the fp64 oracle on a bounded sample (rank 0, N=1).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Summaryformer attn TFLOP/s + frames/s (28 blocks, 6528 keys) vs MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PREFILL = 26                # frames 0..25: from frame 25 on, every read has the full 6,528 keys
+RING = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, target_s):
+    """Times the oracle (fp64, numpy) on served block-steps at 6,528 keys; frames/s extrapolated to 28 blocks."""
+    import numpy as np
+    import sf_inputs
+    from oracle import sf_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    one = dict(wl, n_blocks=1)
+    g = so.Geometry.from_workload(one)
+    orc = so.MemoryReplay(g)
+    for t in range(PREFILL):
+        _, k, v = sf_inputs.frame_tensors(one, 0, 0, t)
+        orc.step(t, {0: (sf_inputs.to_host_bytes(k), sf_inputs.to_host_bytes(v))})
+    frames = []
+    t = PREFILL
+    q, k, v = (sf_inputs.to_host_bytes(x) for x in sf_inputs.frame_tensors(one, 0, 0, t))
+    start = time.perf_counter()
+    n = 0
+    while True:
+        orc.step(t, {0: (k, v)})
+        orc.attend(0, q)
+        n += 1
+        t += 1
+        el = time.perf_counter() - start
+        if el >= target_s or n >= 64:
+            break
+    assert orc.n_keys() == 6528
+    per_block_step = el / n
+    return {
+        "value": 1.0 / (per_block_step * wl["n_blocks"]),
+        "unit": "frames/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} served block-steps at 6528 keys (eviction + record copy + fp64 attention of 1104 "
+                  f"query rows x 16 heads x 64), {el:.1f} s; frames/s extrapolated to 28 blocks",
+        "seconds_per_block_step": per_block_step,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the memory of one session lives on one "
+                                   "device and no multi-GPU path is built; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import compressed_memory_kv_amd as sf
+    import sf_inputs
+
+    wl = sf_inputs.WORKLOADS["rollout"]
+    nb, R, H, D, X = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"], wl["x"]
+    cfg = sf.make_config(**wl)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sess = sf.Session(cfg, device=dev)
+    h = sess.handle
+    out = torch.empty((R, H, D), dtype=torch.float32, device=dev)
+
+    # prefill: frames 0..PREFILL-1 through every block (untimed)
+    for t in range(PREFILL):
+        for b in range(nb):
+            q, k, v = sf_inputs.frame_tensors(wl, 0, b, t, device=dev)
+            sf.sf_step(h, b, t, q, k, v, out, 0.0, stream)
+    ring = [[sf_inputs.frame_tensors(wl, 0, b, PREFILL + i, device=dev) for b in range(nb)] for i in range(RING)]
+    torch.cuda.synchronize()
+
+    def one_frame(t, ev=None):
+        frame = ring[(t - PREFILL) % RING]
+        if ev is not None:
+            ev["evict"][0].record(stream)
+        sf.sf_evict(h, t, stream)
+        if ev is not None:
+            ev["evict"][1].record(stream)
+        for b in range(nb):
+            q, k, v = frame[b]
+            if ev is not None:
+                ev["write"].append(torch.cuda.Event(enable_timing=True))
+                ev["write"][-1].record(stream)
+            sf.sf_write_record(h, b, t, k, v, stream)
+            if ev is not None:
+                ev["attn"].append(torch.cuda.Event(enable_timing=True))
+                ev["attn"][-1].record(stream)
+            sf.sf_attend([h], b, [q], [out], 0.0, stream)
+            if ev is not None:
+                ev["attn_end"].append(torch.cuda.Event(enable_timing=True))
+                ev["attn_end"][-1].record(stream)
+
+    t = PREFILL
+    for _ in range(args.warmup):
+        one_frame(t)
+        t += 1
+    torch.cuda.synchronize()
+    assert sess.view()["n_keys"] == 6528
+
+    events = []
+    start_ev = torch.cuda.Event(enable_timing=True)
+    end_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start_ev.record(stream)
+    for _ in range(args.steps):
+        ev = {"evict": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
+              "write": [], "attn": [], "attn_end": []}
+        one_frame(t, ev)
+        events.append(ev)
+        t += 1
+    end_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start_ev.elapsed_time(end_ev)
+
+    attn_ms = [e["attn"][i].elapsed_time(e["attn_end"][i]) for e in events for i in range(nb)]
+    write_ms = [e["write"][i].elapsed_time(e["attn"][i]) for e in events for i in range(nb)]
+    evict_ms = [e["evict"][0].elapsed_time(e["evict"][1]) for e in events]
+    avg = lambda xs: sum(xs) / len(xs)
+    n_keys = 6528
+    attn_flop = 4.0 * R * n_keys * H * D
+    attn_avg_s = avg(attn_ms) * 1e-3
+    attn_tflops = attn_flop / attn_avg_s / 1e12
+    row_bytes = H * D * 2
+    evict_bytes = nb * 2 * 2 * X * row_bytes   # K and V, read + write, every block
+    write_bytes = 2 * 2 * R * row_bytes        # K and V, read + write, one block
+    evict_gbps = evict_bytes / (avg(evict_ms) * 1e-3) / 1e9
+    write_gbps = write_bytes / (avg(write_ms) * 1e-3) / 1e9
+    frames_per_s = args.steps / (total_ms * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(frames_per_s, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, bf16, resident in HBM)",
+        "config": {"workload": "served rollout, steady state: 28 blocks, 16 heads x 64, 24x42 raw + 96 summary "
+                               "tokens per record, Y=2, W=24, 6528 keys per read; step = eviction + 28 x "
+                               "(record write + attention)",
+                   "blocks": nb, "heads": H, "head_dim": D, "record_rows": R, "keys": n_keys},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "sf_attend (attn_bf16_kernel<64> + split combine)",
+                     "flop_per_launch": attn_flop, "avg_launch_us": round(attn_avg_s * 1e6, 3)},
+        "attn_tflops": round(attn_tflops, 2),
+        "evict_gbps": round(evict_gbps, 1),
+        "evict_frac_hbm": round(evict_gbps / PEAK_HBM_GBPS, 4),
+        "evict_avg_us": round(avg(evict_ms) * 1e3, 3),
+        "write_gbps": round(write_gbps, 1),
+        "write_avg_us": round(avg(write_ms) * 1e3, 3),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

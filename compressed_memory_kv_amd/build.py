@@ -1,0 +1,81 @@
+"""Builds libsf.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc.
+
+Usage: python -m compressed_memory_kv_amd.build  (or build() from Python).
+Every HIP file is compiled for gfx950 only, with packed fp32 VALU ops turned
+off, then linked into compressed_memory_kv_amd/libsf.so next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsf.so")
+SOURCES = ["sf_host.cpp", "sf_copy.hip", "sf_attn.hip"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libsf.so")
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compiles every source and links libsf.so; returns its path.  Always recompiles."""
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="sfbuild_")
+    try:
+        procs = []
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            objs.append(obj)
+            lang = ["-x", "hip"]
+            cmd = [cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            if len(procs) >= jobs:
+                _drain(procs)
+        _drain(procs)
+        out_tmp = LIB + ".tmp"
+        cmd = [cc, *COMMON_FLAGS, "-shared", *objs, "-o", out_tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout)
+        os.replace(out_tmp, LIB)
+        return LIB
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def _drain(procs):
+    errors = []
+    while procs:
+        src, p = procs.pop(0)
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            errors.append(f"{src}:\n{out}")
+        elif out and "warning" in out and "packed-fp32-ops" not in out:
+            sys.stderr.write(out)
+    if errors:
+        raise RuntimeError("compile failed:\n" + "\n".join(errors))
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

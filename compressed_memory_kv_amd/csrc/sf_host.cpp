@@ -1,0 +1,552 @@
+// Host side of the C-ABI: config checks, the slot map and fill state of each
+// session, ordering rules, and kernel enqueue.  No device memory is ever
+// allocated here; every pointer comes from the caller.
+//
+// Model card "GTA world model: weights and inference code":
+//   "A frame is a record"       record(t) = H*W raw rows then X summary rows.
+//   "What a frame attends to"   frame t sees itself, the Y frames before it
+//                               whole, older frames inside the window W as
+//                               summaries, and frame 0 whole.
+//   "One buffer, no mask"       Z0 | RAW (Y+1 records) | SUM ((W-Y) x X rows);
+//                               the figure "The buffer one frame apart" fixes
+//                               the rotation (frame 31 takes frame 28's RAW
+//                               place, frame 28's summary takes frame 6's SUM
+//                               place), read here as RAW slot t mod (Y+1) and
+//                               SUM slot f mod (W-Y) for the summarised frame f.
+//   "The rest of the model"     the clean pass rewrites the frame's entry.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sf_internal.h"
+
+namespace {
+
+thread_local std::string g_thread_error;
+
+constexpr int64_t kMaxRowsPerBuffer = (int64_t)1 << 30;
+constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 40;
+
+int64_t elem_bytes(int32_t dtype) { return dtype == SF_BF16 ? 2 : 4; }
+
+struct Geo {
+  int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, total;
+};
+
+sf_status check_config(const sf_config* c, std::string* why) {
+  if (!c) { *why = "config is NULL"; return SF_E_ARG; }
+  if (c->hw < 1 || c->x < 1 || c->y < 0 || c->w <= c->y || c->n_heads < 1 || c->n_blocks < 1 ||
+      c->max_frames < 0) {
+    *why = "config needs hw >= 1, x >= 1, y >= 0, w > y, n_heads >= 1, n_blocks >= 1, max_frames >= 0";
+    return SF_E_ARG;
+  }
+  if (c->dtype != SF_F32 && c->dtype != SF_BF16) { *why = "dtype must be SF_F32 or SF_BF16"; return SF_E_ARG; }
+  if (c->head_dim != 64 && c->head_dim != 128) { *why = "head_dim must be 64 or 128"; return SF_E_UNSUPPORTED; }
+  if (c->y + 1 > 4096 || c->w - c->y > (1 << 20) || c->n_blocks > 4096 || c->n_heads > 4096) {
+    *why = "config too large (y+1 <= 4096, w-y <= 2^20, n_blocks <= 4096, n_heads <= 4096)";
+    return SF_E_UNSUPPORTED;
+  }
+  const int64_t R = (int64_t)c->hw + c->x;
+  const int64_t C = R * (c->y + 2) + (int64_t)(c->w - c->y) * c->x;
+  if (R > (1 << 24) || C > kMaxRowsPerBuffer || C * c->n_heads * (int64_t)c->head_dim > kMaxElemsPerBlockTensor) {
+    *why = "buffer rows exceed the supported range";
+    return SF_E_UNSUPPORTED;
+  }
+  return SF_OK;
+}
+
+Geo geometry(const sf_config* c) {
+  Geo g;
+  g.R = (int64_t)c->hw + c->x;
+  g.C = g.R * (c->y + 2) + (int64_t)(c->w - c->y) * c->x;
+  g.row_elems = (int64_t)c->n_heads * c->head_dim;
+  g.tensor_bytes = g.C * g.row_elems * elem_bytes(c->dtype);
+  g.block_stride = 2 * g.tensor_bytes;
+  g.kv_bytes = g.block_stride * c->n_blocks;
+  g.scratch_off = (g.kv_bytes + 255) / 256 * 256;
+  g.scratch_bytes = c->dtype == SF_BF16 ? (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim) : 0;
+  g.total = g.scratch_off + g.scratch_bytes;
+  return g;
+}
+
+// Slot map and fill state of one session.
+struct Slots {
+  int64_t t_cur = -1;
+  int64_t evicted_for = -1;
+  std::vector<int64_t> raw_frame;  // frame in each RAW slot, -1 empty
+  std::vector<int64_t> sum_frame;  // frame summarised in each SUM slot, -1 empty
+};
+
+struct Segs {
+  int n = 0;
+  int64_t begin[SF_MAX_SEGMENTS] = {0, 0, 0, 0};
+  int64_t len[SF_MAX_SEGMENTS] = {0, 0, 0, 0};
+  int64_t keys = 0;
+};
+
+// Filled rows as ascending contiguous segments: Z0, occupied RAW slots,
+// occupied SUM slots, merged where they touch.
+bool readable(const sf_config& c, const Geo& g, const Slots& s, Segs* out) {
+  Segs r;
+  if (s.t_cur < 0) { *out = r; return true; }
+  auto add = [&](int64_t lo, int64_t hi) -> bool {
+    if (r.n > 0 && r.begin[r.n - 1] + r.len[r.n - 1] == lo) {
+      r.len[r.n - 1] += hi - lo;
+    } else {
+      if (r.n == SF_MAX_SEGMENTS) return false;
+      r.begin[r.n] = lo;
+      r.len[r.n] = hi - lo;
+      ++r.n;
+    }
+    r.keys += hi - lo;
+    return true;
+  };
+  if (!add(0, g.R)) return false;
+  for (int sl = 0; sl <= c.y; ++sl)
+    if (s.raw_frame[sl] >= 1 && !add(g.R * (1 + sl), g.R * (2 + sl))) return false;
+  const int64_t base = g.R * (c.y + 2);
+  for (int u = 0; u < c.w - c.y; ++u)
+    if (s.sum_frame[u] >= 1 && !add(base + (int64_t)u * c.x, base + (int64_t)(u + 1) * c.x)) return false;
+  *out = r;
+  return true;
+}
+
+}  // namespace
+
+struct sf_buffer {
+  sf_config cfg;
+  Geo geo;
+  char* mem = nullptr;
+  bool dry = false;
+  Slots slots;
+  std::vector<int64_t> written_at;  // per block: newest frame written, -1 none
+  bool fail_next = false;
+  std::string err;
+};
+
+namespace {
+
+sf_status fail(sf_buffer* b, sf_status s, const std::string& msg) {
+  g_thread_error = msg;
+  if (b) b->err = msg;
+  return s;
+}
+
+sf_status hip_fail(sf_buffer* b, hipError_t e, const char* what) {
+  return fail(b, SF_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool all_written(const sf_buffer* b, int64_t t) {
+  for (int64_t w : b->written_at)
+    if (w != t) return false;
+  return true;
+}
+
+// Test hook check: consumes the injected failure.
+bool take_injected(sf_buffer* b) {
+  if (!b->fail_next) return false;
+  b->fail_next = false;
+  return true;
+}
+
+// ---- eviction ------------------------------------------------------------
+struct EvictPlan {
+  bool copy = false;
+  int s = -1;
+  int u = -1;
+  int64_t f = -1;
+};
+
+sf_status check_evict(sf_buffer* b, int64_t t, EvictPlan* plan, bool* noop) {
+  const sf_config& c = b->cfg;
+  *noop = false;
+  if (c.max_frames > 0 && t >= c.max_frames) return fail(b, SF_E_RANGE, "frame id at or beyond max_frames");
+  if (t < 0) return fail(b, SF_E_ARG, "negative frame id");
+  if (t != b->slots.t_cur + 1) return fail(b, SF_E_ORDER, "sf_evict(t) needs t == t_cur + 1");
+  if (b->slots.t_cur >= 0 && !all_written(b, b->slots.t_cur))
+    return fail(b, SF_E_ORDER, "sf_evict: some block has not been written at the current frame");
+  if (b->slots.evicted_for == t) { *noop = true; return SF_OK; }
+  EvictPlan p;
+  if (t > c.y) {
+    const int s = (int)(t % (c.y + 1));
+    const int64_t f = b->slots.raw_frame[s];
+    if (f >= 1) {
+      p.copy = true;
+      p.s = s;
+      p.f = f;
+      p.u = (int)(f % (c.w - c.y));
+    }
+  }
+  *plan = p;
+  return SF_OK;
+}
+
+sf_status apply_evict(sf_buffer* b, int64_t t, const EvictPlan& p, hipStream_t st) {
+  const sf_config& c = b->cfg;
+  if (p.copy && take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+  if (p.copy && !b->dry) {
+    const int64_t eb = elem_bytes(c.dtype);
+    const int64_t row_bytes = b->geo.row_elems * eb;
+    const int64_t src = (b->geo.R * (1 + p.s) + c.hw) * row_bytes;
+    const int64_t dst = (b->geo.R * (c.y + 2) + (int64_t)p.u * c.x) * row_bytes;
+    hipError_t e = sf::launch_evict(b->mem, c.n_blocks, (size_t)b->geo.block_stride, (size_t)b->geo.tensor_bytes,
+                                    (size_t)src, (size_t)dst, (size_t)(c.x * row_bytes), st);
+    if (e != hipSuccess) return hip_fail(b, e, "evict launch");
+  }
+  if (p.copy) b->slots.sum_frame[p.u] = p.f;
+  b->slots.evicted_for = t;
+  return SF_OK;
+}
+
+// ---- record write ---------------------------------------------------------
+sf_status check_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, bool assume_evicted) {
+  const sf_config& c = b->cfg;
+  if (block < 0 || block >= c.n_blocks) return fail(b, SF_E_ARG, "block index out of range");
+  if (t < 0) return fail(b, SF_E_ARG, "negative frame id");
+  if (c.max_frames > 0 && t >= c.max_frames) return fail(b, SF_E_RANGE, "frame id at or beyond max_frames");
+  if (!b->dry && (!k || !v)) return fail(b, SF_E_ARG, "k or v is NULL");
+  if (t == b->slots.t_cur) return SF_OK;  // rewrite of the current frame (clean pass)
+  if (t != b->slots.t_cur + 1) return fail(b, SF_E_ORDER, "sf_write_record(t) needs t == t_cur or t_cur + 1");
+  if (b->slots.t_cur >= 0 && !all_written(b, b->slots.t_cur))
+    return fail(b, SF_E_ORDER, "advance before every block holds the current frame");
+  if (t >= 1) {
+    const int s = (int)(t % (c.y + 1));
+    const int64_t f = b->slots.raw_frame[s];
+    if (f >= 1 && b->slots.evicted_for != t && !assume_evicted)
+      return fail(b, SF_E_ORDER, "the frame leaving this RAW slot has not been evicted (call sf_evict first)");
+  }
+  return SF_OK;
+}
+
+sf_status apply_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st) {
+  const sf_config& c = b->cfg;
+  const int64_t row_bytes = b->geo.row_elems * elem_bytes(c.dtype);
+  const int64_t row0 = t == 0 ? 0 : b->geo.R * (1 + t % (c.y + 1));
+  if (take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+  if (!b->dry) {
+    char* kb = b->mem + block * b->geo.block_stride + row0 * row_bytes;
+    char* vb = kb + b->geo.tensor_bytes;
+    hipError_t e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
+    if (e != hipSuccess) return hip_fail(b, e, "write launch");
+  }
+  if (t != b->slots.t_cur) {
+    b->slots.t_cur = t;
+    if (t >= 1) b->slots.raw_frame[t % (c.y + 1)] = t;
+  }
+  b->written_at[block] = t;
+  return SF_OK;
+}
+
+// ---- attention -------------------------------------------------------------
+sf_status check_attend_one(sf_buffer* b, int32_t block, bool after_write) {
+  if (block < 0 || block >= b->cfg.n_blocks) return fail(b, SF_E_ARG, "block index out of range");
+  if (!after_write && (b->slots.t_cur < 0 || b->written_at[block] != b->slots.t_cur))
+    return fail(b, SF_E_STATE, "sf_attend: the block does not hold the current frame");
+  return SF_OK;
+}
+
+sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
+                         float scale, hipStream_t st) {
+  sf_buffer* b0 = bufs[0];
+  const sf_config& c0 = b0->cfg;
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c0.head_dim);
+  const float scale_log2 = sc * 1.4426950408889634f;
+  for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
+    const int cnt = n - first < sf::kMaxLaunchSessions ? n - first : sf::kMaxLaunchSessions;
+    sf::AttnLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.n_sessions = cnt;
+    a.n_heads = c0.n_heads;
+    a.head_dim = c0.head_dim;
+    a.scale_log2 = scale_log2;
+    const bool bf16 = c0.dtype == SF_BF16;
+    const int rows_per_tile = bf16 ? sf::kBf16RowsPerTile : sf::kF32RowsPerTile;
+    // Key split: aim at about four workgroups per compute unit for the launch.
+    int64_t base_units = 0, total_tiles = 0;
+    std::vector<Segs> segs(cnt);
+    for (int i = 0; i < cnt; ++i) {
+      sf_buffer* b = bufs[first + i];
+      readable(b->cfg, b->geo, b->slots, &segs[i]);
+      const int64_t qt = (b->geo.R + rows_per_tile - 1) / rows_per_tile;
+      base_units += qt * c0.n_heads;
+      total_tiles += qt * c0.n_heads * ((segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile);
+    }
+    const int64_t target_units = 1024;
+    int64_t tiles_per_unit = (total_tiles + target_units - 1) / target_units;
+    if (tiles_per_unit < 4) tiles_per_unit = 4;
+    int64_t units = 0;
+    for (int i = 0; i < cnt; ++i) {
+      sf_buffer* b = bufs[first + i];
+      sf::AttnSession& s = a.s[i];
+      s.q = q[first + i];
+      s.out = static_cast<float*>(out[first + i]);
+      s.k = b->mem + block * b->geo.block_stride;
+      s.v = b->mem + block * b->geo.block_stride + b->geo.tensor_bytes;
+      s.part_o = reinterpret_cast<float*>(b->mem + b->geo.scratch_off);
+      s.part_ml = s.part_o + (size_t)sf::kMaxSplit * b->geo.R * c0.n_heads * c0.head_dim;
+      s.rows = (int32_t)b->geo.R;
+      s.n_keys = (int32_t)segs[i].keys;
+      s.n_seg = segs[i].n;
+      for (int j = 0; j < segs[i].n; ++j) {
+        s.seg_begin[j] = (int32_t)segs[i].begin[j];
+        s.seg_len[j] = (int32_t)segs[i].len[j];
+      }
+      s.qtiles = (int32_t)((b->geo.R + rows_per_tile - 1) / rows_per_tile);
+      int64_t split = 1;
+      if (bf16) {
+        const int64_t tiles = (segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile;
+        split = (tiles + tiles_per_unit - 1) / tiles_per_unit;
+        if (split > sf::kMaxSplit) split = sf::kMaxSplit;
+        if (split > tiles) split = tiles;
+        if (split < 1) split = 1;
+      }
+      s.split = (int32_t)split;
+      s.unit_begin = (int32_t)units;
+      units += (int64_t)s.qtiles * c0.n_heads * split;
+    }
+    (void)base_units;
+    if (units >= ((int64_t)1 << 30)) return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
+    a.total_units = (int32_t)units;
+    hipError_t e = bf16 ? sf::launch_attend_bf16(a, st) : sf::launch_attend_f32(a, st);
+    if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
+    if (bf16) {
+      e = sf::launch_combine(a, st);
+      if (e != hipSuccess) return hip_fail(b0, e, "combine launch");
+    }
+  }
+  return SF_OK;
+}
+
+void fill_view(const sf_config& c, const Geo& g, const Slots& s, int32_t blocks_written, sf_view* v) {
+  Segs r;
+  readable(c, g, s, &r);
+  v->t_cur = s.t_cur;
+  v->n_keys = r.keys;
+  v->evicted_for = s.evicted_for;
+  v->n_seg = r.n;
+  v->raw_slot = s.t_cur >= 1 ? (int32_t)(s.t_cur % (c.y + 1)) : -1;
+  v->blocks_written = blocks_written;
+  v->reserved = 0;
+  for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
+    v->seg_begin[i] = i < r.n ? r.begin[i] : 0;
+    v->seg_len[i] = i < r.n ? r.len[i] : 0;
+  }
+  if (v->raw_frame)
+    for (int i = 0; i <= c.y; ++i) v->raw_frame[i] = s.raw_frame[i];
+  if (v->sum_frame)
+    for (int i = 0; i < c.w - c.y; ++i) v->sum_frame[i] = s.sum_frame[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+sf_status sf_config_check(const sf_config* cfg) {
+  std::string why;
+  sf_status s = check_config(cfg, &why);
+  if (s != SF_OK) g_thread_error = why;
+  return s;
+}
+
+size_t sf_buffer_bytes(const sf_config* cfg) {
+  std::string why;
+  if (check_config(cfg, &why) != SF_OK) return 0;
+  return (size_t)geometry(cfg).total;
+}
+
+size_t sf_kv_bytes(const sf_config* cfg) {
+  std::string why;
+  if (check_config(cfg, &why) != SF_OK) return 0;
+  return (size_t)geometry(cfg).kv_bytes;
+}
+
+int64_t sf_kv_offset(const sf_config* cfg, int32_t block, int32_t which) {
+  std::string why;
+  if (check_config(cfg, &why) != SF_OK || block < 0 || block >= cfg->n_blocks || (which != 0 && which != 1))
+    return -1;
+  const Geo g = geometry(cfg);
+  return block * g.block_stride + which * g.tensor_bytes;
+}
+
+sf_status sf_buffer_create(const sf_config* cfg, void* dev_mem, size_t bytes, void* hip_stream, sf_buffer** out) {
+  std::string why;
+  if (!out) return fail(nullptr, SF_E_ARG, "out is NULL");
+  *out = nullptr;
+  sf_status st = check_config(cfg, &why);
+  if (st != SF_OK) return fail(nullptr, st, why);
+  const Geo g = geometry(cfg);
+  const bool dry = dev_mem == nullptr && bytes == 0;
+  if (!dry) {
+    if (!dev_mem) return fail(nullptr, SF_E_ARG, "dev_mem is NULL but bytes > 0");
+    if (bytes < (size_t)g.total) return fail(nullptr, SF_E_ARG, "device memory smaller than sf_buffer_bytes(cfg)");
+    if (reinterpret_cast<uintptr_t>(dev_mem) & 15u) return fail(nullptr, SF_E_ARG, "device memory not 16-byte aligned");
+  }
+  sf_buffer* b = new (std::nothrow) sf_buffer();
+  if (!b) return fail(nullptr, SF_E_ARG, "out of host memory");
+  b->cfg = *cfg;
+  b->geo = g;
+  b->mem = static_cast<char*>(dev_mem);
+  b->dry = dry;
+  b->slots.raw_frame.assign(cfg->y + 1, -1);
+  b->slots.sum_frame.assign(cfg->w - cfg->y, -1);
+  b->written_at.assign(cfg->n_blocks, -1);
+  if (!dry) {
+    hipError_t e = sf::launch_fill_zero(dev_mem, (size_t)g.kv_bytes, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) {
+      delete b;
+      return fail(nullptr, SF_E_HIP, std::string("zero fill launch: ") + hipGetErrorString(e));
+    }
+  }
+  *out = b;
+  return SF_OK;
+}
+
+sf_status sf_buffer_destroy(sf_buffer* buf) {
+  delete buf;
+  return SF_OK;
+}
+
+sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* k, const void* v, void* hip_stream) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  sf_status s = check_write(buf, block, t, k, v, false);
+  if (s != SF_OK) return s;
+  return apply_write(buf, block, t, k, v, static_cast<hipStream_t>(hip_stream));
+}
+
+sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  EvictPlan p;
+  bool noop = false;
+  sf_status s = check_evict(buf, t, &p, &noop);
+  if (s != SF_OK || noop) return s;
+  return apply_evict(buf, t, p, static_cast<hipStream_t>(hip_stream));
+}
+
+sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
+                    float scale, void* hip_stream) {
+  if (!bufs || n < 1 || n > SF_MAX_BATCH) return fail(nullptr, SF_E_ARG, "sf_attend: need 1 <= n <= SF_MAX_BATCH");
+  if (!bufs[0]) return fail(nullptr, SF_E_ARG, "sf_attend: NULL buffer");
+  const sf_config& c0 = bufs[0]->cfg;
+  const bool dry = bufs[0]->dry;
+  if (!dry && (!q || !out)) return fail(bufs[0], SF_E_ARG, "sf_attend: q or out array is NULL");
+  if (!(scale == scale) || std::isinf(scale)) return fail(bufs[0], SF_E_ARG, "sf_attend: scale is not finite");
+  for (int i = 0; i < n; ++i) {
+    sf_buffer* b = bufs[i];
+    if (!b) return fail(bufs[0], SF_E_ARG, "sf_attend: NULL buffer");
+    if (b->dry != dry) return fail(bufs[0], SF_E_ARG, "sf_attend: dry-run and real buffers mixed");
+    if (b->cfg.n_heads != c0.n_heads || b->cfg.head_dim != c0.head_dim || b->cfg.dtype != c0.dtype)
+      return fail(bufs[0], SF_E_ARG, "sf_attend: sessions differ in n_heads, head_dim or dtype");
+    for (int j = 0; j < i; ++j)
+      if (bufs[j] == b) return fail(bufs[0], SF_E_ARG, "sf_attend: a session is listed twice");
+    sf_status s = check_attend_one(b, block, false);
+    if (s != SF_OK) return fail(bufs[0], s, b->err);
+    if (!dry && (!q[i] || !out[i])) return fail(bufs[0], SF_E_ARG, "sf_attend: q or out pointer is NULL");
+  }
+  for (int i = 0; i < n; ++i)
+    if (take_injected(bufs[i])) return fail(bufs[0], SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+  if (dry) return SF_OK;
+  return enqueue_attend(bufs, n, block, q, out, scale, static_cast<hipStream_t>(hip_stream));
+}
+
+sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k, const void* v, void* out,
+                  float scale, void* hip_stream) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (!buf->dry && (!q || !out)) return fail(buf, SF_E_ARG, "sf_step: q or out is NULL");
+  if (!(scale == scale) || std::isinf(scale)) return fail(buf, SF_E_ARG, "sf_step: scale is not finite");
+  // Validate every part before enqueueing anything.
+  EvictPlan ep;
+  bool evict_due = false, noop = true;
+  if (t == buf->slots.t_cur + 1 && t >= 1) {
+    sf_status s = check_evict(buf, t, &ep, &noop);
+    if (s != SF_OK) return s;
+    evict_due = !noop;
+  }
+  sf_status s = check_write(buf, block, t, k, v, evict_due);
+  if (s != SF_OK) return s;
+  s = check_attend_one(buf, block, true);
+  if (s != SF_OK) return s;
+  const Slots saved = buf->slots;
+  const std::vector<int64_t> saved_written = buf->written_at;
+  auto restore = [&](sf_status r) {
+    buf->slots = saved;
+    buf->written_at = saved_written;
+    return r;
+  };
+  if (evict_due) {
+    s = apply_evict(buf, t, ep, st);
+    if (s != SF_OK) return restore(s);
+  }
+  s = apply_write(buf, block, t, k, v, st);
+  if (s != SF_OK) return restore(s);
+  if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
+  if (buf->dry) return SF_OK;
+  sf_buffer* one[1] = {buf};
+  const void* qs[1] = {q};
+  void* outs[1] = {out};
+  s = enqueue_attend(one, 1, block, qs, outs, scale, st);
+  if (s != SF_OK) return restore(s);
+  return SF_OK;
+}
+
+sf_status sf_query(const sf_buffer* buf, sf_view* view) {
+  if (!buf || !view) return fail(nullptr, SF_E_ARG, "sf_query: NULL argument");
+  int32_t nw = 0;
+  for (int64_t w : buf->written_at) nw += (buf->slots.t_cur >= 0 && w == buf->slots.t_cur);
+  fill_view(buf->cfg, buf->geo, buf->slots, nw, view);
+  return SF_OK;
+}
+
+sf_status sf_plan(const sf_config* cfg, int64_t t, sf_view* view) {
+  std::string why;
+  if (!view) return fail(nullptr, SF_E_ARG, "sf_plan: view is NULL");
+  sf_status st = check_config(cfg, &why);
+  if (st != SF_OK) return fail(nullptr, st, why);
+  if (t < -1) return fail(nullptr, SF_E_ARG, "sf_plan: t < -1");
+  if (cfg->max_frames > 0 && t >= cfg->max_frames) return fail(nullptr, SF_E_RANGE, "frame id at or beyond max_frames");
+  if (t > ((int64_t)1 << 32)) return fail(nullptr, SF_E_UNSUPPORTED, "sf_plan: t too large");
+  const Geo g = geometry(cfg);
+  Slots s;
+  s.raw_frame.assign(cfg->y + 1, -1);
+  s.sum_frame.assign(cfg->w - cfg->y, -1);
+  for (int64_t f = 0; f <= t; ++f) {
+    if (f > cfg->y) {
+      const int sl = (int)(f % (cfg->y + 1));
+      const int64_t leaving = s.raw_frame[sl];
+      if (leaving >= 1) s.sum_frame[leaving % (cfg->w - cfg->y)] = leaving;
+    }
+    if (f >= 1) s.raw_frame[f % (cfg->y + 1)] = f;
+    if (f >= 1) s.evicted_for = f;
+    s.t_cur = f;
+  }
+  fill_view(*cfg, g, s, t >= 0 ? cfg->n_blocks : 0, view);
+  return SF_OK;
+}
+
+const char* sf_status_str(sf_status s) {
+  switch (s) {
+    case SF_OK: return "SF_OK";
+    case SF_E_ARG: return "SF_E_ARG";
+    case SF_E_ORDER: return "SF_E_ORDER";
+    case SF_E_RANGE: return "SF_E_RANGE";
+    case SF_E_STATE: return "SF_E_STATE";
+    case SF_E_HIP: return "SF_E_HIP";
+    case SF_E_UNSUPPORTED: return "SF_E_UNSUPPORTED";
+  }
+  return "SF_E_UNKNOWN";
+}
+
+const char* sf_last_error(const sf_buffer* buf) { return buf ? buf->err.c_str() : g_thread_error.c_str(); }
+
+sf_status sf_debug_fail_next_launch(sf_buffer* buf) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  buf->fail_next = true;
+  return SF_OK;
+}
+
+}  // extern "C"

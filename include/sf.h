@@ -1,0 +1,180 @@
+/*
+ * sf.h - C-ABI of the Summaryformer per-block memory, native on MI355X (gfx950).
+ *
+ * The method is described on the model card titled "GTA world model: weights
+ * and inference code" (Summaryformer).  Citations below name its sections:
+ *   [record]   "A frame is a record": a frame's record is its H*W raw tokens
+ *              followed by its X summary tokens (the record(t) equation).
+ *   [attends]  "What a frame attends to": the four-item list of what frame
+ *              t's tokens see.
+ *   [buffer]   "One buffer, no mask": one preallocated K/V buffer per block,
+ *              laid out Z0 | RAW | SUM; the eviction paragraph; the figure
+ *              "The buffer one frame apart"; the parameter table; the single
+ *              dense, unmasked read of the filled rows.
+ *   [sampling] "The rest of the model", item "Sampling": a clean pass
+ *              rewrites the frame's entry in memory.
+ *   [limits]   "Limits": sessions end at the last frame id of the position
+ *              table (4096 ids on the page).
+ *
+ * Terms.  A session is one player's memory: n_blocks independent buffers,
+ * one per transformer block, stepped together frame by frame.  R = hw + x
+ * rows per record; capacity C = R*(y+2) + (w-y)*x rows per buffer:
+ *   Z0        rows [0, R)                        record of frame 0 (start image)
+ *   RAW s     rows [R*(1+s), R*(2+s))            s = t mod (y+1), frame t >= 1
+ *   SUM u     rows [R*(y+2)+u*x, R*(y+2)+(u+1)*x) u = f mod (w-y), summary of frame f
+ *
+ * Memory.  The caller owns all device memory.  One session needs
+ * sf_buffer_bytes(cfg) bytes of device memory, which it hands to
+ * sf_buffer_create; the library never allocates device memory.  That memory
+ * holds, for block b = 0..n_blocks-1, K_b then V_b, each [C][n_heads][head_dim]
+ * row-major in the config's dtype (so byte offset of K_b is
+ * b * 2 * C*n_heads*head_dim*elem, V_b follows K_b); after the last block
+ * comes a scratch region that sf_attend uses for partial results of this
+ * session.  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
+ *
+ * Tensors passed per call (device pointers, row-major, contiguous):
+ *   q, k, v : [R][n_heads][head_dim] in the config dtype (fp32 or bf16)
+ *   out     : [R][n_heads][head_dim] fp32
+ *
+ * Ordering and state.  All device work is enqueued on the given HIP stream
+ * (NULL = the default stream) with no host synchronisation; host state
+ * advances at enqueue.  All of one session's calls must use one stream (or
+ * be ordered by the caller).  A handle is not thread-safe.  Every call that
+ * returns an error leaves the host state unchanged and enqueues nothing,
+ * except SF_E_HIP raised by a launch after an earlier launch of the same call
+ * was enqueued: the host state is restored, but device contents of the rows
+ * that call touches are then undefined.
+ *
+ * Dry-run handles.  sf_buffer_create with dev_mem == NULL and bytes == 0
+ * makes a handle that validates and advances state exactly like a real one
+ * but never touches a device; its device-pointer arguments may be NULL.
+ *
+ * Errors never throw; sf_last_error gives a message.
+ */
+#ifndef SF_H
+#define SF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sf_status {
+  SF_OK = 0,
+  SF_E_ARG = -1,          /* bad argument: NULL pointer, bad index, bad config, short memory */
+  SF_E_ORDER = -2,        /* call out of order for the session's frame sequence */
+  SF_E_RANGE = -3,        /* frame id at or beyond max_frames */
+  SF_E_STATE = -4,        /* handle not in a state that allows the call */
+  SF_E_HIP = -5,          /* a HIP runtime call or kernel launch failed */
+  SF_E_UNSUPPORTED = -6   /* valid but not implemented (e.g. head_dim other than 64/128) */
+} sf_status;
+
+typedef enum sf_dtype { SF_F32 = 0, SF_BF16 = 1 } sf_dtype;
+
+/* Shape of one session ([record], [buffer] parameter table). */
+typedef struct sf_config {
+  int32_t hw;         /* raw tokens per frame: one per latent grid cell (H*W), >= 1 */
+  int32_t x;          /* summary tokens per frame (X), >= 1 */
+  int32_t y;          /* frames kept whole before the current one (Y), >= 0 */
+  int32_t w;          /* memory window in frames (W), > y */
+  int32_t n_heads;    /* attention heads (K/V heads = Q heads), >= 1 */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t n_blocks;   /* transformer blocks, one buffer each, >= 1 */
+  int32_t dtype;      /* sf_dtype of q, k, v and of the stored K/V */
+  int64_t max_frames; /* frame ids must stay below this ([limits]); 0 = no cap */
+} sf_config;
+
+#define SF_MAX_SEGMENTS 4
+#define SF_MAX_BATCH 64
+
+/* Host-side snapshot of one session's slot map and fill state. */
+typedef struct sf_view {
+  int64_t t_cur;        /* newest frame id written; -1 before the first write */
+  int64_t n_keys;       /* rows the next attend reads (sum of seg_len) */
+  int64_t evicted_for;  /* frame id whose eviction step last ran; -1 if none */
+  int32_t n_seg;        /* readable row segments, ascending, <= SF_MAX_SEGMENTS */
+  int32_t raw_slot;     /* RAW slot of t_cur; -1 while t_cur <= 0 */
+  int32_t blocks_written; /* blocks whose record for t_cur has been written */
+  int32_t reserved;
+  int64_t seg_begin[SF_MAX_SEGMENTS];
+  int64_t seg_len[SF_MAX_SEGMENTS];
+  int64_t* raw_frame;   /* in: caller array of y+1 entries or NULL; out: frame id per RAW slot (-1 empty) */
+  int64_t* sum_frame;   /* in: caller array of w-y entries or NULL; out: frame id per SUM slot (-1 empty) */
+} sf_view;
+
+typedef struct sf_buffer sf_buffer;
+
+/* Checks a config; SF_OK, SF_E_ARG (inconsistent) or SF_E_UNSUPPORTED. */
+sf_status sf_config_check(const sf_config* cfg);
+
+/* Device bytes one session needs (K/V of all blocks + attend scratch); 0 if cfg is invalid. */
+size_t sf_buffer_bytes(const sf_config* cfg);
+
+/* Canonical K/V bytes (a prefix of the session memory): n_blocks * 2 * C*n_heads*head_dim*elem. */
+size_t sf_kv_bytes(const sf_config* cfg);
+
+/* Byte offset of block b's K (which = 0) or V (which = 1) in the session memory; -1 if invalid. */
+int64_t sf_kv_offset(const sf_config* cfg, int32_t block, int32_t which);
+
+/* [buffer] One preallocated buffer per block.  Binds dev_mem (>= sf_buffer_bytes, 16-byte
+ * aligned, owned by the caller, valid until destroy and until enqueued work ends) to a new
+ * handle and enqueues a zero fill of the K/V bytes on stream, so empty slots read as zero.
+ * dev_mem == NULL with bytes == 0 makes a dry-run handle. */
+sf_status sf_buffer_create(const sf_config* cfg, void* dev_mem, size_t bytes, void* hip_stream,
+                           sf_buffer** out);
+
+/* Frees the host handle only (the device memory stays the caller's). NULL is allowed. */
+sf_status sf_buffer_destroy(sf_buffer* buf);
+
+/* [buffer], [sampling] Copies record(t)'s K and V of one block into Z0 (t = 0) or RAW slot
+ * t mod (y+1).  t must be t_cur (a rewrite: last write wins) or t_cur + 1 (an advance, allowed
+ * once every block holds t_cur and the frame leaving that RAW slot has been evicted).  k and v
+ * are device pointers to [R][n_heads][head_dim] in the config dtype. */
+sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* k, const void* v,
+                          void* hip_stream);
+
+/* [buffer] eviction paragraph.  Before frame t is written: copies K and V of the x summary rows
+ * (record rows [hw, R)) of the frame leaving RAW slot t mod (y+1) into its SUM slot
+ * f mod (w-y), in every block, in one launch.  The raw rows are not copied.  t must be
+ * t_cur + 1 with every block holding t_cur.  A no-op when no generated frame leaves (t <= y+1);
+ * repeating it for the same t is a no-op. */
+sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
+
+/* [attends], [buffer] The dense read.  For each of n sessions (n <= SF_MAX_BATCH; equal
+ * n_heads, head_dim and dtype; block < n_blocks in each): out[i] = softmax(scale * q K^T) V over
+ * every filled row of that session's block buffer, per head, for all R query rows; no mask.
+ * scale <= 0 means 1/sqrt(head_dim).  Each session's block must hold its t_cur (SF_E_STATE
+ * otherwise).  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
+ * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One launch
+ * (plus a combine launch when the key range is split) for the whole batch. */
+sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
+                    void* const* out, float scale, void* hip_stream);
+
+/* One block of one frame: sf_evict(t) if it is due and has not run, then sf_write_record,
+ * then sf_attend of this session alone. */
+sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k,
+                  const void* v, void* out, float scale, void* hip_stream);
+
+/* Host snapshot of the slot map and fill state; no device work. */
+sf_status sf_query(const sf_buffer* buf, sf_view* view);
+
+/* The view a session has after stepping frames 0..t in order (every block written each
+ * frame, evictions as due); t = -1 gives the empty state.  Pure host arithmetic. */
+sf_status sf_plan(const sf_config* cfg, int64_t t, sf_view* view);
+
+/* Static name of a status code. */
+const char* sf_status_str(sf_status s);
+
+/* Message of the last error on buf (NULL buf: of the calling thread's last failed call). */
+const char* sf_last_error(const sf_buffer* buf);
+
+/* Test hook: the next device launch made through buf fails with SF_E_HIP before launching. */
+sf_status sf_debug_fail_next_launch(sf_buffer* buf);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_H */

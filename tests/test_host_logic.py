@@ -1,0 +1,246 @@
+"""Host logic of libsf on the CPU: exports, slot map against the oracle, ordering and error rules.
+
+No device work: dry-run handles (dev_mem NULL) validate and advance state like
+real ones without touching a GPU.  Page: model card "GTA world model: weights
+and inference code", section "One buffer, no mask".
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import compressed_memory_kv_amd as sf
+import sf_inputs
+from oracle import sf_oracle as so
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "sf.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"\b(sf_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 14
+    lib = sf._lib
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/sf.h but not exported by libsf.so"
+    assert set(names) == set(sf.EXPORTED)
+
+
+def test_exports_via_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", sf.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (sf_[a-z_0-9]+)$", out, re.M))
+    assert set(header_functions()) <= exported
+
+
+GEOMS = {
+    "tiny": sf_inputs.WORKLOADS["tiny"],
+    "served": sf_inputs.WORKLOADS["rollout"],
+    "long": sf_inputs.WORKLOADS["long"],
+    "odd": dict(hw=5, x=3, y=1, w=4, n_heads=2, head_dim=64, n_blocks=3, dtype="bf16"),
+    "y0": dict(hw=7, x=2, y=0, w=3, n_heads=1, head_dim=128, n_blocks=2, dtype="f32"),
+}
+
+
+def oracle_tables(wl, t_last):
+    g = so.Geometry(wl["hw"], wl["x"], wl["y"], wl["w"], 1, 1, 1, "f32")
+    m = so.MemoryReplay(g)
+    one = np.zeros((g.r, 1, 1), np.float32)
+    for t in range(t_last + 1):
+        m.step(t, {0: (one, one)})
+        yield t, m
+
+
+@pytest.mark.parametrize("name", list(GEOMS))
+def test_plan_matches_oracle(name):
+    wl = GEOMS[name]
+    cfg = sf.make_config(**wl)
+    empty = sf.sf_plan(cfg, -1)
+    assert empty["t_cur"] == -1 and empty["n_keys"] == 0 and empty["segments"] == []
+    t_last = 140 if name != "long" else 110
+    for t, m in oracle_tables(wl, t_last):
+        p = sf.sf_plan(cfg, t)
+        assert p["raw_frame"] == m.raw_frame, t
+        assert p["sum_frame"] == m.sum_frame, t
+        assert p["segments"] == m.readable_segments(), t
+        assert p["n_keys"] == m.n_keys() == so.key_count(so.Geometry.from_workload(dict(wl)), t)
+        assert p["t_cur"] == t
+        assert p["raw_slot"] == (t % (wl["y"] + 1) if t >= 1 else -1)
+
+
+def test_buffer_sizes_and_offsets():
+    wl = sf_inputs.WORKLOADS["rollout"]
+    cfg = sf.make_config(**wl)
+    C = 1104 * 4 + 22 * 96
+    assert C == 6528
+    per_tensor = C * 16 * 64 * 2
+    assert sf.sf_kv_bytes(cfg) == 28 * 2 * per_tensor
+    assert sf.sf_kv_offset(cfg, 0, 0) == 0
+    assert sf.sf_kv_offset(cfg, 0, 1) == per_tensor
+    assert sf.sf_kv_offset(cfg, 5, 1) == 5 * 2 * per_tensor + per_tensor
+    assert sf.sf_kv_offset(cfg, 28, 0) == -1 and sf.sf_kv_offset(cfg, 0, 2) == -1
+    assert sf.sf_buffer_bytes(cfg) >= sf.sf_kv_bytes(cfg)
+    lwl = sf_inputs.WORKLOADS["long"]
+    lcfg = sf.make_config(**lwl)
+    assert sf.sf_kv_bytes(lcfg) == 28 * 2 * 46688 * 24 * 128 * 2
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(hw=0), sf.SF_E_ARG), (dict(x=0), sf.SF_E_ARG), (dict(y=-1), sf.SF_E_ARG), (dict(w=2), sf.SF_E_ARG),
+    (dict(n_heads=0), sf.SF_E_ARG), (dict(n_blocks=0), sf.SF_E_ARG), (dict(dtype=7), sf.SF_E_ARG),
+    (dict(head_dim=96), sf.SF_E_UNSUPPORTED), (dict(max_frames=-1), sf.SF_E_ARG),
+])
+def test_config_errors(bad, code):
+    wl = dict(GEOMS["tiny"])
+    wl.update(bad)
+    cfg = sf.make_config(**wl)
+    with pytest.raises(sf.SfError) as ei:
+        sf.sf_config_check(cfg)
+    assert ei.value.status == code
+    assert sf.sf_buffer_bytes(cfg) == 0
+
+
+def dry_session(name="tiny", **over):
+    wl = dict(GEOMS[name])
+    wl.update(over)
+    return sf.Session(sf.make_config(**wl), dry=True), wl
+
+
+def advance(s, wl, t):
+    for b in range(wl["n_blocks"]):
+        sf.sf_step(s.handle, b, t, None, None, None, None)
+
+
+def test_dry_session_follows_plan():
+    for name in ("tiny", "odd", "y0"):
+        s, wl = dry_session(name)
+        for t in range(40):
+            advance(s, wl, t)
+            v = s.view()
+            p = sf.sf_plan(s.cfg, t)
+            for key in ("t_cur", "n_keys", "segments", "raw_frame", "sum_frame", "evicted_for", "raw_slot"):
+                assert v[key] == p[key], (name, t, key)
+            assert v["blocks_written"] == wl["n_blocks"]
+
+
+def test_explicit_evict_write_attend_sequence():
+    s, wl = dry_session("odd")
+    h = s.handle
+    for t in range(12):
+        if t >= 1:
+            sf.sf_evict(h, t)
+            sf.sf_evict(h, t)  # repeating the eviction for the same frame is a no-op
+        for b in range(wl["n_blocks"]):
+            sf.sf_write_record(h, b, t, None, None)
+            sf.sf_write_record(h, b, t, None, None)  # the clean pass rewrites the entry
+            sf.sf_attend([h], b, None, None)
+        assert s.view() == {**sf.sf_plan(s.cfg, t), "blocks_written": wl["n_blocks"]}
+
+
+def expect(code, fn, *args):
+    with pytest.raises(sf.SfError) as ei:
+        fn(*args)
+    assert ei.value.status == code, (ei.value, code)
+
+
+def test_ordering_errors_leave_state_unchanged():
+    s, wl = dry_session("tiny", max_frames=20)
+    h = s.handle
+    expect(sf.SF_E_STATE, sf.sf_attend, [h], 0, None, None)       # nothing written yet
+    expect(sf.SF_E_ORDER, sf.sf_write_record, h, 0, 1, None, None)  # skipping frame 0
+    for t in range(5):
+        advance(s, wl, t)
+    before = s.view()
+    expect(sf.SF_E_ORDER, sf.sf_write_record, h, 0, 6, None, None)  # skipping a frame
+    expect(sf.SF_E_ORDER, sf.sf_write_record, h, 0, 3, None, None)  # going back
+    expect(sf.SF_E_ORDER, sf.sf_write_record, h, 0, 5, None, None)  # frame 4 leaves RAW unevicted
+    expect(sf.SF_E_ORDER, sf.sf_evict, h, 4)                          # eviction is for t_cur + 1
+    expect(sf.SF_E_ORDER, sf.sf_evict, h, 7)
+    expect(sf.SF_E_ARG, sf.sf_write_record, h, 1, 4, None, None)     # block out of range
+    expect(sf.SF_E_ARG, sf.sf_write_record, h, -1, 4, None, None)
+    expect(sf.SF_E_ARG, sf.sf_attend, [h], 3, None, None)
+    assert s.view() == before
+    for t in range(5, 20):
+        advance(s, wl, t)
+    expect(sf.SF_E_RANGE, sf.sf_evict, h, 20)
+    expect(sf.SF_E_RANGE, sf.sf_write_record, h, 0, 20, None, None)
+    expect(sf.SF_E_RANGE, sf.sf_step, h, 0, 20, None, None, None, None)
+
+
+def test_advance_needs_every_block():
+    s, wl = dry_session("odd")
+    h = s.handle
+    advance(s, wl, 0)
+    sf.sf_write_record(h, 0, 1, None, None)
+    expect(sf.SF_E_ORDER, sf.sf_evict, h, 2)                         # blocks 1, 2 still hold frame 0
+    expect(sf.SF_E_ORDER, sf.sf_write_record, h, 0, 2, None, None)
+    expect(sf.SF_E_STATE, sf.sf_attend, [h], 1, None, None)           # block 1 does not hold frame 1
+    sf.sf_attend([h], 0, None, None)
+
+
+def test_batched_attend_checks():
+    a, wl = dry_session("odd")
+    b, _ = dry_session("odd")
+    c, _ = dry_session("odd", n_heads=4)
+    for s in (a, b, c):
+        advance(s, wl, 0)
+    sf.sf_attend([a.handle, b.handle], 1, None, None)
+    expect(sf.SF_E_ARG, sf.sf_attend, [a.handle, c.handle], 1, None, None)  # heads differ
+    expect(sf.SF_E_ARG, sf.sf_attend, [a.handle, a.handle], 1, None, None)  # listed twice
+    expect(sf.SF_E_ARG, sf.sf_attend, [], 0, None, None)
+    expect(sf.SF_E_ARG, sf.sf_attend, [a.handle] * 65, 0, None, None)
+
+
+def test_injected_launch_failure_keeps_state():
+    s, wl = dry_session("tiny")
+    h = s.handle
+    for t in range(6):
+        advance(s, wl, t)
+    before = s.view()
+    sf.sf_debug_fail_next_launch(h)
+    expect(sf.SF_E_HIP, sf.sf_step, h, 0, 6, None, None, None, None)
+    assert s.view() == before
+    assert "injected" in sf.sf_last_error(h)
+    sf.sf_step(h, 0, 6, None, None, None, None)                      # the next call goes through
+    assert s.view()["t_cur"] == 6
+    sf.sf_debug_fail_next_launch(h)
+    expect(sf.SF_E_HIP, sf.sf_attend, [h], 0, None, None)
+    sf.sf_attend([h], 0, None, None)
+
+
+def test_status_strings():
+    assert sf.sf_status_str(sf.SF_E_ORDER) == "SF_E_ORDER"
+    assert sf.sf_status_str(0) == "SF_OK"
+    assert sf.sf_status_str(-99) == "SF_E_UNKNOWN"
+
+
+@settings(max_examples=150, deadline=None)
+@given(hw=st.integers(1, 40), x=st.integers(1, 12), y=st.integers(0, 5), extra=st.integers(1, 12),
+       t=st.integers(-1, 90))
+def test_plan_properties(hw, x, y, extra, t):
+    w = y + extra
+    cfg = sf.make_config(hw, x, y, w, 1, 64, 1, "f32")
+    p = sf.sf_plan(cfg, t)
+    g = so.Geometry(hw, x, y, w, 1, 1, 1, "f32")
+    if t < 0:
+        assert p["n_keys"] == 0
+        return
+    assert p["n_keys"] == so.key_count(g, t)
+    assert 1 <= len(p["segments"]) <= 2
+    assert sum(n for _, n in p["segments"]) == p["n_keys"]
+    C = g.capacity
+    ends = [b + n for b, n in p["segments"]]
+    assert all(0 <= b < e <= C for (b, _), e in zip(p["segments"], ends))
+    frames = [f for f in p["raw_frame"] if f >= 0] + [f for f in p["sum_frame"] if f >= 0]
+    assert len(frames) == len(set(frames))                         # slots disjoint
+    assert set(f for f in p["raw_frame"] if f >= 1) == set(range(max(1, t - y), t + 1))
+    assert set(f for f in p["sum_frame"] if f >= 1) == set(range(max(1, t - w), t - y))
+    if t >= w + 1:
+        assert p["segments"] == [(0, C)]                           # steady state: one dense prefix
