@@ -291,11 +291,11 @@ class Session:
         sf_step(self.handle, block, t, self._check(q), self._check(k), self._check(v), self._check(out, True),
                 scale, stream)
 
+    def view(self) -> dict:
+        return sf_query(self.handle, self.cfg)
+
 
 def attend_batch(sessions, block, qs, outs, scale=0.0, stream=None):
     """One batched sf_attend over several Session objects, with each tensor checked."""
     sf_attend([s.handle for s in sessions], block, [s._check(q) for s, q in zip(sessions, qs)],
               [s._check(o, True) for s, o in zip(sessions, outs)], scale, stream)
-
-    def view(self) -> dict:
-        return sf_query(self.handle, self.cfg)
