@@ -16,6 +16,7 @@ stream the library launches on, around each call inside the timed region.
 The cpu_baseline leg times the fp64 oracle on a bounded sample (rank 0, N=1).
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -114,26 +115,32 @@ def main():
     ring = [[sf_inputs.frame_tensors(wl, 0, b, PREFILL + i, device=dev) for b in range(nb)] for i in range(RING)]
     torch.cuda.synchronize()
 
+    # Pre-marshalled pointers and pre-created events keep the host ahead of the GPU.
+    lib = sf._lib
+    sptr = stream.cuda_stream
+    hs = (ctypes.c_void_p * 1)(h)
+    ring_ptrs = [[(q.data_ptr(), k.data_ptr(), v.data_ptr()) for (q, k, v) in frame] for frame in ring]
+    qarr = [[(ctypes.c_void_p * 1)(p[0]) for p in frame] for frame in ring_ptrs]
+    oarr = (ctypes.c_void_p * 1)(out.data_ptr())
+
     def one_frame(t, ev=None):
-        frame = ring[(t - PREFILL) % RING]
+        i = (t - PREFILL) % RING
+        frame = ring_ptrs[i]
         if ev is not None:
-            ev["evict"][0].record(stream)
-        sf.sf_evict(h, t, stream)
+            ev[0].record(stream)
+        rc = lib.sf_evict(h, t, sptr)
         if ev is not None:
-            ev["evict"][1].record(stream)
+            ev[1].record(stream)
         for b in range(nb):
-            q, k, v = frame[b]
+            _, kp, vp = frame[b]
+            rc |= lib.sf_write_record(h, b, t, kp, vp, sptr)
             if ev is not None:
-                ev["write"].append(torch.cuda.Event(enable_timing=True))
-                ev["write"][-1].record(stream)
-            sf.sf_write_record(h, b, t, k, v, stream)
+                ev[2 + 2 * b].record(stream)
+            rc |= lib.sf_attend(hs, 1, b, qarr[i][b], oarr, 0.0, sptr)
             if ev is not None:
-                ev["attn"].append(torch.cuda.Event(enable_timing=True))
-                ev["attn"][-1].record(stream)
-            sf.sf_attend([h], b, [q], [out], 0.0, stream)
-            if ev is not None:
-                ev["attn_end"].append(torch.cuda.Event(enable_timing=True))
-                ev["attn_end"][-1].record(stream)
+                ev[3 + 2 * b].record(stream)
+        if rc != 0:
+            raise RuntimeError("libsf call failed: " + sf.sf_last_error(h))
 
     t = PREFILL
     for _ in range(args.warmup):
@@ -142,26 +149,23 @@ def main():
     torch.cuda.synchronize()
     assert sess.view()["n_keys"] == 6528
 
-    events = []
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * nb)] for _ in range(args.steps)]
     start_ev = torch.cuda.Event(enable_timing=True)
     end_ev = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start_ev.record(stream)
-    for _ in range(args.steps):
-        ev = {"evict": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
-              "write": [], "attn": [], "attn_end": []}
-        one_frame(t, ev)
-        events.append(ev)
+    for s_i in range(args.steps):
+        one_frame(t, events[s_i])
         t += 1
     end_ev.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start_ev.elapsed_time(end_ev)
 
-    attn_ms = [e["attn"][i].elapsed_time(e["attn_end"][i]) for e in events for i in range(nb)]
-    write_ms = [e["write"][i].elapsed_time(e["attn"][i]) for e in events for i in range(nb)]
-    evict_ms = [e["evict"][0].elapsed_time(e["evict"][1]) for e in events]
+    attn_ms = [e[2 + 2 * b].elapsed_time(e[3 + 2 * b]) for e in events for b in range(nb)]
+    write_ms = [(e[1] if b == 0 else e[1 + 2 * b]).elapsed_time(e[2 + 2 * b]) for e in events for b in range(nb)]
+    evict_ms = [e[0].elapsed_time(e[1]) for e in events]
     avg = lambda xs: sum(xs) / len(xs)
     n_keys = 6528
     attn_flop = 4.0 * R * n_keys * H * D

@@ -17,7 +17,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsf.so")
+# SF_LIB_PATH points the binding at another build of the same C-ABI (e.g. a tuning build).
+LIB_PATH = os.environ.get("SF_LIB_PATH") or os.path.join(_HERE, "libsf.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m compressed_memory_kv_amd.build` "

@@ -16,7 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsf.so")
-SOURCES = ["sf_host.cpp", "sf_copy.hip", "sf_attn.hip"]
+SOURCES = ["sf_host.cpp", "sf_copy.hip", "sf_attn.hip", "sf_attn_sk.hip"]
+# Per-file code generation flags.  The attention kernels: MFMA results stay in
+# VGPRs (no AGPR round trips), and IEEE mode is off so max chains become v_max3
+# (no NaN canonicalisation; the kernels compute nothing on NaN inputs).
+FILE_FLAGS = {
+    "sf_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"],
+    "sf_attn_sk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"],
+}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -44,7 +51,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"]
-            cmd = [cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON_FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

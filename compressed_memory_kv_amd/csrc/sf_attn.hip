@@ -45,6 +45,7 @@ namespace sf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -54,21 +55,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int BM = kBf16RowsPerTile;  // 128 query rows per workgroup
 constexpr int BN = kBf16KeysPerTile;  // 64 keys per tile
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the reference max moves
 static_assert(BM == kWaves * 32, "one 32-row MFMA block per wave");
-
-// Flattened key index -> buffer row, walking the readable segments in order.
-__device__ __forceinline__ int key_row(const AttnSession& s, int kappa) {
-  int r = kappa;
-#pragma unroll
-  for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
-    if (i < s.n_seg) {
-      if (r < s.seg_len[i]) return s.seg_begin[i] + r;
-      r -= s.seg_len[i];
-    }
-  }
-  return 0;  // not reached for kappa < n_keys
-}
 
 // Work unit of this workgroup: XCD-aware remap of blockIdx.x.
 __device__ __forceinline__ int unit_of_block() {
@@ -76,102 +63,182 @@ __device__ __forceinline__ int unit_of_block() {
   return (int)(blockIdx.x & 7u) * per_xcd + (int)(blockIdx.x >> 3);
 }
 
-__device__ __forceinline__ int session_of_unit(const AttnLaunch& a, int unit) {
+// Everything a workgroup needs about its unit, wave-uniform (held in SGPRs).
+struct Unit {
+  const char* q;
+  float* out;
+  const char* k;
+  const char* v;
+  float* part_o;
+  float* part_ml;
+  int rows, n_keys, split, ks, qt, h;
+  int seg_row[SF_MAX_SEGMENTS];  // first buffer row of segment i
+  int seg_key[SF_MAX_SEGMENTS];  // first flattened key of segment i (INT_MAX when unused)
+};
+
+// Decodes unit -> (session, head, query tile, key split).  Units of one launch are
+// numbered session by session, then head, then query tile, then split.
+__device__ __forceinline__ Unit decode_unit(const AttnLaunch& a, int unit, bool with_split) {
   int si = 0;
   for (int i = 1; i < a.n_sessions; ++i)
     if (a.s[i].unit_begin <= unit) si = i;
-  return si;
+  si = __builtin_amdgcn_readfirstlane(si);
+  const AttnSession& S = a.s[si];
+  Unit u;
+  u.q = reinterpret_cast<const char*>(S.q);
+  u.out = S.out;
+  u.k = reinterpret_cast<const char*>(S.k);
+  u.v = reinterpret_cast<const char*>(S.v);
+  u.part_o = S.part_o;
+  u.part_ml = S.part_ml;
+  u.rows = S.rows;
+  u.n_keys = S.n_keys;
+  u.split = with_split ? S.split : 1;
+  // Integer division is emulated on the VALU; readfirstlane puts the (uniform) results back in SGPRs.
+  int local = unit - S.unit_begin;
+  u.ks = __builtin_amdgcn_readfirstlane(local % u.split);
+  local = __builtin_amdgcn_readfirstlane(local / u.split);
+  u.qt = __builtin_amdgcn_readfirstlane(local % S.qtiles);
+  u.h = __builtin_amdgcn_readfirstlane(local / S.qtiles);
+  int cum = 0;
+#pragma unroll
+  for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
+    const bool used = i < S.n_seg;
+    u.seg_row[i] = used ? S.seg_begin[i] : 0;
+    u.seg_key[i] = used ? cum : 0x7fffffff;
+    cum += used ? S.seg_len[i] : 0;
+  }
+  return u;
+}
+
+// Flattened key index -> buffer row (branch-free walk over the segments).
+__device__ __forceinline__ int key_row(const Unit& u, int kappa) {
+  int row = u.seg_row[0] + kappa;
+#pragma unroll
+  for (int i = 1; i < SF_MAX_SEGMENTS; ++i)
+    row = kappa >= u.seg_key[i] ? u.seg_row[i] + (kappa - u.seg_key[i]) : row;
+  return row;
 }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// LDS tile geometry: one stage holds a K tile then a V tile, BN rows of 2D bytes
+// each, as 16-byte chunks permuted within each row so that the MFMA operand
+// reads are bank-conflict free:
+//   K: chunk c of row r sits at c ^ (r & 7)      (ds_read_b128: eight lanes read
+//      eight consecutive rows at one chunk -> eight distinct 16-byte groups);
+//   V: chunk c of row r sits at c ^ 2*(r & 3)    (ds_read_b64_tr_b16: a 16-lane
+//      group reads four consecutive rows x 32 bytes -> four disjoint 32-byte groups).
 template <int D>
-struct Bf16Smem {
-  uint4 k[2][BN * D / 8];  // [buffer][row * D/8 + swizzled 16-byte chunk]
-  uint4 v[2][BN * D / 8];  // [buffer][row * D/8 + swizzled 16-byte chunk, 32-byte XOR]
+struct Tile {
+  static constexpr int ROW = 2 * D;              // bytes per row
+  static constexpr int KBYTES = BN * ROW;
+  static constexpr int STAGE = 2 * KBYTES;       // K tile then V tile
 };
+
+// Probability sums above this make the tile recompute against its true max: every
+// p stays <= 2^15 in the accumulators, and p of the first tile (reference -inf) is inf.
+constexpr float kSumLimit = 32768.0f;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a) {
+  using T = Tile<D>;
   constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
   constexpr int PER = BN * CH / kThreads;    // chunks per thread per tensor per tile
   constexpr int KSTEPS = D / 16;             // MFMA k-steps over head_dim
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
   static_assert(PER * kThreads == BN * CH, "tile loads divide evenly");
-  __shared__ Bf16Smem<D> sm;
+  __shared__ __attribute__((aligned(16))) char sm[2 * T::STAGE];
 
   const int unit = unit_of_block();
   if (unit >= a.total_units) return;
-  const AttnSession& S = a.s[session_of_unit(a, unit)];
+  const Unit U = decode_unit(a, unit, true);
   const int H = a.n_heads;
-  int local = unit - S.unit_begin;
-  const int split = S.split;
-  const int ks = local % split;
-  local /= split;
-  const int qt = local % S.qtiles;
-  const int h = local / S.qtiles;
-  const int ntiles = (S.n_keys + BN - 1) / BN;
-  const int t0 = (int)((long long)ks * ntiles / split);
-  const int t1 = (int)((long long)(ks + 1) * ntiles / split);
-  const int key_hi = min(t1 * BN, S.n_keys);
+  const int ntiles = (U.n_keys + BN - 1) / BN;
+  const int t0 = __builtin_amdgcn_readfirstlane((int)((long long)U.ks * ntiles / U.split));
+  const int t1 = __builtin_amdgcn_readfirstlane((int)((long long)(U.ks + 1) * ntiles / U.split));
+  const int key_hi = min(t1 * BN, U.n_keys);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5;   // lane half: k-group of MFMA operands
   const int l32 = lane & 31; // query of this lane within the wave's block
-  const int qrow = qt * BM + wave * 32 + l32;
-  const bool row_ok = qrow < S.rows;
-  const bool wave_on = qt * BM + wave * 32 < S.rows;
+  const int qrow = U.qt * BM + wave * 32 + l32;
+  const bool row_ok = qrow < U.rows;
+  const bool wave_on = U.qt * BM + wave * 32 < U.rows;  // wave-uniform
   const float c = a.scale_log2;
+  const int row_stride = H * D;       // elements per buffer row
+  const int row_bytes = 2 * row_stride;
 
-  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(S.k);
-  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(S.v);
-  const size_t row_stride = (size_t)H * D;
-
-  // Q^T operand: lane holds Q[qrow][16*kk + 8*g .. +7] for every k-step.
+  // Q^T operand: lane holds Q[qrow][16*kk + 8*g .. +7] for every k-step (rows past R read row R-1).
   bf16x8 qreg[KSTEPS];
   {
-    const __bf16* qp = reinterpret_cast<const __bf16*>(S.q) + (size_t)qrow * row_stride + (size_t)h * D + 8 * g;
+    const int qoff = min(qrow, U.rows - 1) * row_stride + U.h * D + 8 * g;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(U.q) + qoff;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (row_ok) {
-        qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qreg[kk][i] = (__bf16)0.0f;
-      }
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
   }
 
-  uint4 kr[PER], vr[PER];
-  auto load_tile = [&](int tile) {
+  // Per-thread tile-load geometry (loop invariant).  Chunk p of this thread is row
+  // tid/CH + p*RSTEP, chunk tid%CH; rows p*RSTEP apart share (row & 7), so every
+  // chunk's global and LDS offsets are those of chunk 0 plus a constant.
+  constexpr int RSTEP = kThreads / CH;
+  static_assert(RSTEP % 8 == 0, "chunks of one thread share their swizzle");
+  const char* __restrict__ kg = U.k + 2 * U.h * D;
+  const char* __restrict__ vg = U.v + 2 * U.h * D;
+  const int prow = tid / CH;
+  const unsigned goff = (unsigned)(prow * row_bytes + (tid % CH) * 16);
+  const unsigned gstep = (unsigned)(RSTEP * row_bytes);
+  const int ksoff = prow * T::ROW + (((tid % CH) ^ (prow & 7)) << 4);
+  const int vsoff = T::KBYTES + prow * T::ROW + (((tid % CH) ^ (2 * (prow & 3))) << 4);
+  // Per-lane LDS operand addresses (bytes within a stage).
+  int kaddr[KSTEPS];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int ci = tid + p * kThreads;
-      const int row = ci / CH;
-      const int cc = ci % CH;
-      const int kappa = tile * BN + row;
-      if (kappa < key_hi) {
-        const size_t off = (size_t)key_row(S, kappa) * row_stride + (size_t)h * D + cc * 8;
-        kr[p] = *reinterpret_cast<const uint4*>(kg + off);
-        vr[p] = *reinterpret_cast<const uint4*>(vg + off);
-      } else {
-        kr[p] = make_uint4(0u, 0u, 0u, 0u);
-        vr[p] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = l32 * T::ROW + (((2 * kk + g) ^ (l32 & 7)) << 4);
+  const int trow = (lane >> 2) & 3;
+  int vaddr[DBLK];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int ci = tid + p * kThreads;
-      const int row = ci / CH;
-      const int cc = ci % CH;
-      sm.k[buf][row * CH + (cc ^ (row & 7))] = kr[p];
-      sm.v[buf][row * CH + ((((cc >> 1) ^ (row & 3)) << 1) | (cc & 1))] = vr[p];
-    }
-  };
+  for (int db = 0; db < DBLK; ++db) {
+    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    vaddr[db] = T::KBYTES + (4 * g + trow) * T::ROW + ((chunk ^ (2 * trow)) << 4) + 8 * (lane & 1);
+  }
+
+  // Loads tile TILE into staging registers KR/VR.  A tile inside one segment is a
+  // run of rows: a scalar base plus the fixed per-thread offsets.  Otherwise each
+  // row is looked up; keys past the unit's range re-read its last key (finite
+  // data) and get score -inf.
+#define SF_LOAD_TILE(TILE, KR, VR)                                                          \
+  {                                                                                         \
+    const int kap0_ = (TILE) * BN;                                                          \
+    int srow_ = U.seg_row[0], skey_ = U.seg_key[0], send_ = U.seg_key[1];                   \
+    _Pragma("unroll") for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {                           \
+      const bool in_ = kap0_ >= U.seg_key[i];                                               \
+      srow_ = in_ ? U.seg_row[i] : srow_;                                                   \
+      skey_ = in_ ? U.seg_key[i] : skey_;                                                   \
+      send_ = in_ ? (i + 1 < SF_MAX_SEGMENTS ? U.seg_key[i + 1 < SF_MAX_SEGMENTS ? i + 1 : i] : 0x7fffffff) : send_; \
+    }                                                                                       \
+    if (kap0_ + BN <= min(send_, key_hi)) {                                                 \
+      const unsigned base_ = (unsigned)((srow_ + kap0_ - skey_) * row_bytes);               \
+      _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                     \
+        KR[p] = *reinterpret_cast<const u32x4*>(kg + base_ + p * gstep + goff);             \
+        VR[p] = *reinterpret_cast<const u32x4*>(vg + base_ + p * gstep + goff);             \
+      }                                                                                     \
+    } else {                                                                                \
+      _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                     \
+        const int kappa_ = min(kap0_ + prow + p * RSTEP, key_hi - 1);                       \
+        const unsigned off_ = (unsigned)(key_row(U, kappa_) * row_bytes) + (tid % CH) * 16; \
+        KR[p] = *reinterpret_cast<const u32x4*>(kg + off_);                                 \
+        VR[p] = *reinterpret_cast<const u32x4*>(vg + off_);                                 \
+      }                                                                                     \
+    }                                                                                       \
+  }
+#define SF_STORE_TILE(STAGE_BYTES, KR, VR)                                                  \
+  _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                         \
+    *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + ksoff + p * RSTEP * T::ROW) = KR[p];     \
+    *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + vsoff + p * RSTEP * T::ROW) = VR[p];     \
+  }
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -180,62 +247,35 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mref = -INFINITY;  // reference max, log2 units
   float lsum = 0.0f;       // this lane's share of the row sum
-
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int tile = t0; tile < t1; ++tile) {
-    const int buf = (tile - t0) & 1;
-    const bool more = tile + 1 < t1;
-    if (more) load_tile(tile + 1);
-
-    if (wave_on) {
-      const uint4* ks_lds = sm.k[buf];
-      // ---- S^T = K . Q^T : two 32-key blocks
-      f32x16 s0, s1;
+  // One tile of work on the stage at byte offset ST.
+  auto compute_tile = [&](const int tile, const int ST) {
+    const char* st = sm + ST;
+    // ---- S^T = K . Q^T : two 32-key blocks
+    f32x16 s0, s1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int ch = 2 * kk + g;
-        const int r0 = l32, r1 = 32 + l32;
-        const uint4 a0 = ks_lds[r0 * CH + (ch ^ (r0 & 7))];
-        const uint4 a1 = ks_lds[r1 * CH + (ch ^ (r1 & 7))];
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qreg[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qreg[kk], s1, 0, 0, 0);
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kaddr[kk]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + kaddr[kk] + 32 * T::ROW);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+    }
+    // ---- keys past the end of this unit's range (ragged last tile) score -inf
+    if (tile * BN + BN > key_hi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kb = tile * BN + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (kb >= key_hi) s0[r] = -INFINITY;
+        if (kb + 32 >= key_hi) s1[r] = -INFINITY;
       }
-      // ---- keys past the end of this unit's range (ragged last tile) score -inf
-      if (tile * BN + BN > key_hi) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kb = tile * BN + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kb >= key_hi) s0[r] = -INFINITY;
-          if (kb + 32 >= key_hi) s1[r] = -INFINITY;
-        }
-      }
-      // ---- tile max over this query's 64 scores (32 here, 32 in lane^32)
-      float mt = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-      mt = fmaxf(mt, xor32(mt)) * c;
-      const bool need = mt > mref + kLazyRescale;
-      if (__any(need)) {
-        const float mnew = fmaxf(mref, mt);
-        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        lsum *= alpha;
-        mref = mnew;
-      }
-      // ---- P = exp2(S*c - mref), rounded to bf16; row sum of the rounded values
-      bf16x8 pb[4];
+    }
+    // ---- P = exp2(S*c - mref) in bf16 and its row sum, against the current reference.
+    bf16x8 pb[4];
+    float ts;
+    auto probs = [&]() {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         pb[0][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -mref));
@@ -243,45 +283,78 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
         pb[2][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -mref));
         pb[3][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 + r], c, -mref));
       }
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bf16x2 pr = {pb[j][2 * e], pb[j][2 * e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          part[j] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part[j], false);
         }
-      }
-      // ---- O^T += V^T . P^T ; k-step j covers S^T registers 8*(j&1).. of block j>>1,
-      // i.e. keys 32*(j>>1) + 16*(j&1) + {4g..4g+3} then {8+4g..8+4g+3}.
-      const char* vs_lds = reinterpret_cast<const char*>(sm.v[buf]);
-      const int trow = (lane >> 2) & 3;           // row within the 4-row group this lane addresses
-      const int tcol = 4 * (lane & 3);            // column within the 16-column chunk
+      ts = (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    probs();
+    // ---- the reference moves only when some p left its range, and on the unit's first
+    // tile (the reference is -inf before it; masked keys there give NaN p, discarded here).
+    if (tile == t0 || __any(ts > kSumLimit)) {
+      float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int chunk32 = 2 * db + ((lane >> 4) & 1);
+      for (int r = 1; r < 16; ++r) mt = max3(mt, s0[r], s1[r]);
+      mt = fmaxf(mt, xor32(mt)) * c;
+      const float mnew = fmaxf(mref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kb = 32 * (j >> 1) + 16 * (j & 1) + 4 * g;
-          const int ra = kb + trow, rb = kb + 8 + trow;
-          const int ea = ra * D + (((chunk32 ^ (ra & 3)) << 4) | tcol);
-          const int eb = rb * D + (((chunk32 ^ (rb & 3)) << 4) | tcol);
-          const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_lds + 2 * ea));
-          const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_lds + 2 * eb));
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j], o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      lsum *= alpha;
+      mref = mnew;
+      probs();
+    }
+    lsum += ts;
+    // ---- O^T += V^T . P^T ; k-step j covers S^T registers 8*(j&1).. of block j>>1,
+    // i.e. keys 32*(j>>1) + 16*(j&1) + {4g..4g+3} then {8+4g..8+4g+3}.
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int roff = (32 * (j >> 1) + 16 * (j & 1)) * T::ROW;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff));
+        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff + 8 * T::ROW));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j], o[db], 0, 0, 0);
       }
     }
+  };
 
-    if (more) store_tile(buf ^ 1);
+  // Pipeline: tile i is computed from stage i&1 while tile i+2 is in flight in one
+  // register set and tile i+1 (the other set) is stored to stage (i+1)&1 after it.
+  u32x4 kra[PER], vra[PER], krb[PER], vrb[PER];
+  SF_LOAD_TILE(t0, kra, vra)
+  if (t0 + 1 < t1) SF_LOAD_TILE(t0 + 1, krb, vrb)
+  SF_STORE_TILE(0, kra, vra)
+  __syncthreads();
+  for (int tile = t0; tile < t1; tile += 2) {
+    // even step: compute stage 0, refill set a with tile+2, store set b (tile+1) to stage 1
+    if (tile + 2 < t1) SF_LOAD_TILE(tile + 2, kra, vra)
+    if (wave_on) compute_tile(tile, 0);
+    if (tile + 1 < t1) SF_STORE_TILE(T::STAGE, krb, vrb)
+    __syncthreads();
+    if (tile + 1 >= t1) break;
+    // odd step: compute stage 1, refill set b with tile+3, store set a (tile+2) to stage 0
+    if (tile + 3 < t1) SF_LOAD_TILE(tile + 3, krb, vrb)
+    if (wave_on) compute_tile(tile + 1, T::STAGE);
+    if (tile + 2 < t1) SF_STORE_TILE(0, kra, vra)
     __syncthreads();
   }
+#undef SF_LOAD_TILE
+#undef SF_STORE_TILE
 
   if (!wave_on) return;
   const float ltot = lsum + xor32(lsum);
-  const size_t obase = (size_t)qrow * row_stride + (size_t)h * D;
-  if (split == 1) {
-    if (!row_ok) return;
+  const size_t obase = (size_t)qrow * row_stride + (size_t)U.h * D;
+  if (!row_ok) return;
+  if (U.split == 1) {
     const float inv = 1.0f / ltot;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -290,11 +363,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
         const int d = 32 * db + 8 * q4 + 4 * g;
         float4 w = make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
                                o[db][4 * q4 + 3] * inv);
-        *reinterpret_cast<float4*>(S.out + obase + d) = w;
+        *reinterpret_cast<float4*>(U.out + obase + d) = w;
       }
   } else {
-    if (!row_ok) return;
-    float* po = S.part_o + (size_t)ks * S.rows * row_stride + obase;
+    float* po = U.part_o + (size_t)U.ks * U.rows * row_stride + obase;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -304,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
             make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
       }
     if (g == 0) {
-      float* pm = S.part_ml + ((size_t)ks * S.rows * H + (size_t)qrow * H + h) * 2;
+      float* pm = U.part_ml + ((size_t)U.ks * U.rows * H + (size_t)qrow * H + U.h) * 2;
       *reinterpret_cast<float2*>(pm) = make_float2(mref, ltot);
     }
   }
@@ -350,41 +422,33 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
   __shared__ float vs[KT][D];
   const int unit = (int)blockIdx.x;
   if (unit >= a.total_units) return;
-  const AttnSession& S = a.s[session_of_unit(a, unit)];
+  const Unit U = decode_unit(a, unit, false);
   const int H = a.n_heads;
-  const int local = unit - S.unit_begin;
-  const int qt = local % S.qtiles;
-  const int h = local / S.qtiles;
   const int tid = threadIdx.x;
-  const int qrow = qt * kF32RowsPerTile + tid;
-  const bool row_ok = qrow < S.rows;
-  const size_t row_stride = (size_t)H * D;
-  const float* __restrict__ kg = reinterpret_cast<const float*>(S.k);
-  const float* __restrict__ vg = reinterpret_cast<const float*>(S.v);
+  const int qrow = U.qt * kF32RowsPerTile + tid;
+  const bool row_ok = qrow < U.rows;
+  const int row_stride = H * D;
+  const float* __restrict__ kg = reinterpret_cast<const float*>(U.k) + U.h * D;
+  const float* __restrict__ vg = reinterpret_cast<const float*>(U.v) + U.h * D;
   const float c = a.scale_log2;
+  const int n_keys = U.n_keys;
 
   float q[D], o[D];
   {
-    const float* qp = reinterpret_cast<const float*>(S.q) + (size_t)(row_ok ? qrow : 0) * row_stride + (size_t)h * D;
+    const float* qp = reinterpret_cast<const float*>(U.q) + min(qrow, U.rows - 1) * row_stride + U.h * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      q[d] = row_ok ? qp[d] : 0.0f;
+      q[d] = qp[d];
       o[d] = 0.0f;
     }
   }
   float m = -INFINITY, l = 0.0f;
-  for (int base = 0; base < S.n_keys; base += KT) {
+  for (int base = 0; base < n_keys; base += KT) {
     for (int e = tid; e < KT * D; e += kF32Threads) {
       const int j = e / D, d = e % D;
-      const int kappa = base + j;
-      float kv = 0.0f, vv = 0.0f;
-      if (kappa < S.n_keys) {
-        const size_t off = (size_t)key_row(S, kappa) * row_stride + (size_t)h * D + d;
-        kv = kg[off];
-        vv = vg[off];
-      }
-      ks[j][d] = kv;
-      vs[j][d] = vv;
+      const int off = key_row(U, min(base + j, n_keys - 1)) * row_stride + d;
+      ks[j][d] = kg[off];
+      vs[j][d] = vg[off];
     }
     __syncthreads();
     float s[KT];
@@ -394,7 +458,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
       float acc = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], ks[j][d], acc);
-      s[j] = (base + j < S.n_keys) ? acc * c : -INFINITY;
+      s[j] = (base + j < n_keys) ? acc * c : -INFINITY;
       mt = fmaxf(mt, s[j]);
     }
     const float mnew = fmaxf(m, mt);
@@ -413,7 +477,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
     __syncthreads();
   }
   if (!row_ok) return;
-  float* op = S.out + (size_t)qrow * row_stride + (size_t)h * D;
+  float* op = U.out + qrow * row_stride + U.h * D;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;

@@ -6,67 +6,77 @@
 // "One buffer, no mask": a frame's record is written into its RAW place and,
 // when the frame leaves the raw window, only the K/V of its summary rows are
 // copied into SUM; that copy is all it costs to move a frame into long-term
-// memory.  All of these are HBM-bound copies: 16-byte vector loads and
-// stores, four in flight per thread, 64-bit indexing.
+// memory.  These are HBM-bound copies.  Each thread moves kVec 16-byte
+// vectors; the loads of a thread are all issued before its first store (no
+// branches between them), so every wave keeps kVec loads in flight.  Only
+// the last workgroup of a copy takes the bounds-checked path.
 #include "sf_internal.h"
 
 namespace sf {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+constexpr int kVec = 4;
+constexpr size_t kPerBlock = (size_t)kThreads * kVec;  // vectors per workgroup
 
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint4* __restrict__ p, size_t n16) {
-  size_t i = (size_t)blockIdx.x * kThreads * kVecPerThread + threadIdx.x;
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j, i += kThreads)
-    if (i < n16) p[i] = z;
+__device__ __forceinline__ void copy_chunk(u32x4* __restrict__ d, const u32x4* __restrict__ s, size_t first,
+                                           size_t n16) {
+  const size_t i = first + threadIdx.x;
+  if (first + kPerBlock <= n16) {
+    // the source is not read again: stream it past the caches
+    const u32x4 a0 = __builtin_nontemporal_load(s + i);
+    const u32x4 a1 = __builtin_nontemporal_load(s + i + kThreads);
+    const u32x4 a2 = __builtin_nontemporal_load(s + i + 2 * kThreads);
+    const u32x4 a3 = __builtin_nontemporal_load(s + i + 3 * kThreads);
+    d[i] = a0;
+    d[i + kThreads] = a1;
+    d[i + 2 * kThreads] = a2;
+    d[i + 3 * kThreads] = a3;
+  } else {
+    for (size_t j = i; j < n16; j += kThreads) d[j] = s[j];
+  }
 }
 
-// Two independent copies of n16 16-byte vectors (K and V) in one launch:
-// the first half of the grid copies K, the second half V.
-__global__ __launch_bounds__(kThreads) void copy_pair_kernel(uint4* __restrict__ dk, uint4* __restrict__ dv,
-                                                             const uint4* __restrict__ sk,
-                                                             const uint4* __restrict__ sv, size_t n16,
-                                                             unsigned blocks_per_tensor) {
-  const bool second = blockIdx.x >= blocks_per_tensor;
-  const unsigned b = second ? blockIdx.x - blocks_per_tensor : blockIdx.x;
-  uint4* __restrict__ d = second ? dv : dk;
-  const uint4* __restrict__ s = second ? sv : sk;
-  size_t i = (size_t)b * kThreads * kVecPerThread + threadIdx.x;
-  uint4 r[kVecPerThread];
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j)
-    if (i + (size_t)j * kThreads < n16) r[j] = s[i + (size_t)j * kThreads];
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j)
-    if (i + (size_t)j * kThreads < n16) d[i + (size_t)j * kThreads] = r[j];
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(u32x4* __restrict__ p, size_t n16) {
+  const size_t first = (size_t)blockIdx.x * kPerBlock;
+  const size_t i = first + threadIdx.x;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if (first + kPerBlock <= n16) {
+    p[i] = z;
+    p[i + kThreads] = z;
+    p[i + 2 * kThreads] = z;
+    p[i + 3 * kThreads] = z;
+  } else {
+    for (size_t j = i; j < n16; j += kThreads) p[j] = z;
+  }
 }
 
-// Eviction: for every block b and tensor (K, V), copy n16 vectors from
-// src_off to dst_off.  Grid: blocks_per_copy workgroups per (block, tensor).
+// Two copies of n16 vectors (K and V) in one launch: workgroups
+// [0, per) copy K, [per, 2*per) copy V.
+__global__ __launch_bounds__(kThreads) void copy_pair_kernel(u32x4* __restrict__ dk, u32x4* __restrict__ dv,
+                                                             const u32x4* __restrict__ sk,
+                                                             const u32x4* __restrict__ sv, size_t n16,
+                                                             unsigned per) {
+  const bool second = blockIdx.x >= per;
+  const unsigned b = second ? blockIdx.x - per : blockIdx.x;
+  copy_chunk(second ? dv : dk, second ? sv : sk, (size_t)b * kPerBlock, n16);
+}
+
+// Eviction: for every block and tensor (K, V) copy n16 vectors from src_off
+// to dst_off.  Workgroup w serves copy w / per (= 2 * block + tensor).
 __global__ __launch_bounds__(kThreads) void evict_kernel(char* __restrict__ mem, size_t block_stride,
                                                          size_t v_offset, size_t src_off, size_t dst_off,
-                                                         size_t n16, unsigned blocks_per_copy) {
-  const unsigned copy = blockIdx.x / blocks_per_copy;  // = 2 * block + tensor
-  const unsigned b = blockIdx.x - copy * blocks_per_copy;
+                                                         size_t n16, unsigned per) {
+  const unsigned copy = blockIdx.x / per;
+  const unsigned b = blockIdx.x - copy * per;
   char* base = mem + (size_t)(copy >> 1) * block_stride + ((copy & 1u) ? v_offset : 0);
-  const uint4* __restrict__ s = reinterpret_cast<const uint4*>(base + src_off);
-  uint4* __restrict__ d = reinterpret_cast<uint4*>(base + dst_off);
-  size_t i = (size_t)b * kThreads * kVecPerThread + threadIdx.x;
-  uint4 r[kVecPerThread];
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j)
-    if (i + (size_t)j * kThreads < n16) r[j] = s[i + (size_t)j * kThreads];
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j)
-    if (i + (size_t)j * kThreads < n16) d[i + (size_t)j * kThreads] = r[j];
+  copy_chunk(reinterpret_cast<u32x4*>(base + dst_off), reinterpret_cast<const u32x4*>(base + src_off),
+             (size_t)b * kPerBlock, n16);
 }
 
-unsigned blocks_for(size_t n16) {
-  return (unsigned)((n16 + (size_t)kThreads * kVecPerThread - 1) / ((size_t)kThreads * kVecPerThread));
-}
+unsigned blocks_for(size_t n16) { return (unsigned)((n16 + kPerBlock - 1) / kPerBlock); }
 
 }  // namespace
 
@@ -74,11 +84,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;
   if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(p) & 15u)) return hipErrorInvalidValue;
   const size_t n16 = bytes / 16;
-  const size_t per_launch = (size_t)1 << 28;  // vectors per launch keeps the grid well inside 2^31
+  const size_t per_launch = (size_t)1 << 30;  // vectors per launch keeps the grid well inside 2^31
   for (size_t off = 0; off < n16; off += per_launch) {
     const size_t n = n16 - off < per_launch ? n16 - off : per_launch;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, stream,
-                       reinterpret_cast<uint4*>(p) + off, n);
+                       reinterpret_cast<u32x4*>(p) + off, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -92,9 +102,9 @@ hipError_t launch_copy_rows(void* dst_k, void* dst_v, const void* src_k, const v
   const size_t n16 = bytes / 16;
   const unsigned per = blocks_for(n16);
   if ((size_t)per * 2 >= ((size_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_pair_kernel, dim3(per * 2), dim3(kThreads), 0, stream, reinterpret_cast<uint4*>(dst_k),
-                     reinterpret_cast<uint4*>(dst_v), reinterpret_cast<const uint4*>(src_k),
-                     reinterpret_cast<const uint4*>(src_v), n16, per);
+  hipLaunchKernelGGL(copy_pair_kernel, dim3(per * 2), dim3(kThreads), 0, stream, reinterpret_cast<u32x4*>(dst_k),
+                     reinterpret_cast<u32x4*>(dst_v), reinterpret_cast<const u32x4*>(src_k),
+                     reinterpret_cast<const u32x4*>(src_v), n16, per);
   return hipGetLastError();
 }
 

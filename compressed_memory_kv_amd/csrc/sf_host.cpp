@@ -18,6 +18,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -30,7 +31,7 @@ namespace {
 thread_local std::string g_thread_error;
 
 constexpr int64_t kMaxRowsPerBuffer = (int64_t)1 << 30;
-constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 40;
+constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 31;
 
 int64_t elem_bytes(int32_t dtype) { return dtype == SF_BF16 ? 2 : 4; }
 
@@ -53,8 +54,9 @@ sf_status check_config(const sf_config* c, std::string* why) {
   }
   const int64_t R = (int64_t)c->hw + c->x;
   const int64_t C = R * (c->y + 2) + (int64_t)(c->w - c->y) * c->x;
-  if (R > (1 << 24) || C > kMaxRowsPerBuffer || C * c->n_heads * (int64_t)c->head_dim > kMaxElemsPerBlockTensor) {
-    *why = "buffer rows exceed the supported range";
+  // Kernels address one block's K or V (and q, out) with 32-bit element offsets.
+  if (R > (1 << 24) || C > kMaxRowsPerBuffer || C * c->n_heads * (int64_t)c->head_dim >= kMaxElemsPerBlockTensor) {
+    *why = "a block's K or V must hold fewer than 2^31 elements";
     return SF_E_UNSUPPORTED;
   }
   return SF_OK;
@@ -69,7 +71,9 @@ Geo geometry(const sf_config* c) {
   g.block_stride = 2 * g.tensor_bytes;
   g.kv_bytes = g.block_stride * c->n_blocks;
   g.scratch_off = (g.kv_bytes + 255) / 256 * 256;
-  g.scratch_bytes = c->dtype == SF_BF16 ? (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim) : 0;
+  g.scratch_bytes = c->dtype != SF_BF16 ? 0
+                    : c->head_dim == 64 ? (int64_t)sf::sk_scratch_bytes(g.R, c->n_heads, g.C)
+                                        : (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim);
   g.total = g.scratch_off + g.scratch_bytes;
   return g;
 }
@@ -250,12 +254,80 @@ sf_status check_attend_one(sf_buffer* b, int32_t block, bool after_write) {
   return SF_OK;
 }
 
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// bf16, head_dim 64: persistent stream-K kernel, then the combine of split units.
+sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
+                            void* const* out, float scale_log2, hipStream_t st) {
+  sf_buffer* b0 = bufs[0];
+  const int H = b0->cfg.n_heads;
+  for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
+    const int cnt = n - first < sf::kMaxLaunchSessions ? n - first : sf::kMaxLaunchSessions;
+    sf::SkLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.n_sessions = cnt;
+    a.n_heads = H;
+    a.scale_log2 = scale_log2;
+    int64_t iters = 0, units_total = 0;
+    for (int i = 0; i < cnt; ++i) {
+      sf_buffer* b = bufs[first + i];
+      Segs sg;
+      readable(b->cfg, b->geo, b->slots, &sg);
+      sf::SkSession& s = a.s[i];
+      s.q = q[first + i];
+      s.out = static_cast<float*>(out[first + i]);
+      s.k = b->mem + block * b->geo.block_stride;
+      s.v = b->mem + block * b->geo.block_stride + b->geo.tensor_bytes;
+      s.rows = (int32_t)b->geo.R;
+      s.n_keys = (int32_t)sg.keys;
+      s.n_seg = sg.n;
+      for (int j = 0; j < sg.n; ++j) {
+        s.seg_begin[j] = (int32_t)sg.begin[j];
+        s.seg_len[j] = (int32_t)sg.len[j];
+      }
+      s.qtiles = (int32_t)((b->geo.R + sf::kSkRows - 1) / sf::kSkRows);
+      s.ntiles = (int32_t)((sg.keys + sf::kSkKeys - 1) / sf::kSkKeys);
+      s.ppu = sf::sk_pieces_per_unit(b->geo.C);
+      const int64_t units = (int64_t)H * s.qtiles;
+      s.part_o = reinterpret_cast<float*>(b->mem + b->geo.scratch_off);
+      s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
+      s.it_begin = (int32_t)iters;
+      iters += units * s.ntiles;
+      units_total += units;
+    }
+    if (iters >= ((int64_t)1 << 30)) return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
+    int64_t G = device_cu_count();
+    if (G > iters / sf::kSkMinRange) G = iters / sf::kSkMinRange;
+    if (G < 1) G = 1;
+    if (G >= 8) G -= G % 8;
+    a.n_wg = (int32_t)G;
+    a.n_iters = (int32_t)iters;
+    hipError_t e = sf::launch_attend_sk(a, st);
+    if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
+    e = sf::launch_combine_sk(a, (int)units_total, st);
+    if (e != hipSuccess) return hip_fail(b0, e, "combine launch");
+  }
+  return SF_OK;
+}
+
 sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
                          float scale, hipStream_t st) {
   sf_buffer* b0 = bufs[0];
   const sf_config& c0 = b0->cfg;
   const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c0.head_dim);
   const float scale_log2 = sc * 1.4426950408889634f;
+  if (c0.dtype == SF_BF16 && c0.head_dim == 64) return enqueue_attend_sk(bufs, n, block, q, out, scale_log2, st);
   for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
     const int cnt = n - first < sf::kMaxLaunchSessions ? n - first : sf::kMaxLaunchSessions;
     sf::AttnLaunch a;
@@ -279,6 +351,10 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     const int64_t target_units = 1024;
     int64_t tiles_per_unit = (total_tiles + target_units - 1) / target_units;
     if (tiles_per_unit < 4) tiles_per_unit = 4;
+    // SF_ATTN_SPLIT=n forces n key splits per (session, head, query tile) (tuning only:
+    // results change only by rounding).
+    const char* split_env = std::getenv("SF_ATTN_SPLIT");
+    const int forced_split = split_env ? std::atoi(split_env) : 0;
     int64_t units = 0;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
@@ -300,7 +376,7 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
       int64_t split = 1;
       if (bf16) {
         const int64_t tiles = (segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile;
-        split = (tiles + tiles_per_unit - 1) / tiles_per_unit;
+        split = forced_split > 0 ? forced_split : (tiles + tiles_per_unit - 1) / tiles_per_unit;
         if (split > sf::kMaxSplit) split = sf::kMaxSplit;
         if (split > tiles) split = tiles;
         if (split < 1) split = 1;

@@ -44,6 +44,49 @@ struct AttnLaunch {
   AttnSession s[kMaxLaunchSessions];
 };
 
+// ---- persistent stream-K attention (bf16, head_dim 64) ----------------------
+// The launch's work is the flattened sequence of (session, head, 128-row query
+// tile, 64-key tile) iterations; workgroup w takes iterations
+// [w*N/G, (w+1)*N/G).  A query tile that spans several workgroups leaves one
+// partial result per workgroup ("piece") in its session's scratch; the combine
+// kernel merges them.
+constexpr int kSkRows = 128;        // query rows per unit
+constexpr int kSkKeys = 64;         // keys per tile
+constexpr int kSkMinRange = 8;      // fewest tiles a workgroup is given
+struct SkSession {
+  const void* q;        // [rows][H][64] bf16
+  float* out;           // [rows][H][64] fp32
+  const void* k;        // this block's K [C][H][64]
+  const void* v;        // this block's V [C][H][64]
+  float* part_o;        // [units][ppu][kSkRows][64] unnormalised partial numerators
+  float* part_ml;       // [units][ppu][kSkRows][2] (reference max in log2 units, row sum)
+  int32_t rows;         // query rows (R)
+  int32_t n_keys;       // readable rows
+  int32_t n_seg;
+  int32_t qtiles;       // ceil(rows / kSkRows)
+  int32_t ntiles;       // ceil(n_keys / kSkKeys)
+  int32_t ppu;          // piece slots per unit in the scratch
+  int32_t it_begin;     // first iteration of this session in the launch
+  int32_t pad;
+  int32_t seg_begin[SF_MAX_SEGMENTS];
+  int32_t seg_len[SF_MAX_SEGMENTS];
+};
+struct SkLaunch {
+  int32_t n_sessions;
+  int32_t n_heads;
+  int32_t n_wg;         // G
+  int32_t n_iters;      // N
+  float scale_log2;
+  int32_t pad[3];
+  SkSession s[kMaxLaunchSessions];
+};
+// Piece slots per unit a session of capacity C needs (bounded because every
+// workgroup gets at least kSkMinRange tiles).
+int32_t sk_pieces_per_unit(int64_t capacity_rows);
+size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows);
+hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream);
+hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream);
+
 // Query rows per workgroup of each attention kernel.
 constexpr int kBf16RowsPerTile = 128;
 constexpr int kF32RowsPerTile = 256;

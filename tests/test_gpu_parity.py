@@ -93,7 +93,10 @@ def test_tiny_f32_rollout_with_rewrites():
             orc.step(t, {0: (host(k0), host(v0))})
         q, k, v = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
         sess.step(0, t, q, k, v, out)
-        orc.step(t, {0: (host(k), host(v))})
+        if t in (4, 9):
+            orc.write(0, t, host(k), host(v))  # the rewrite: no second eviction
+        else:
+            orc.step(t, {0: (host(k), host(v))})
         torch.cuda.synchronize()
         check_tables(sess, orc, f"tiny t={t}")
         check_buffer(sess, orc, 0, f"tiny t={t}")
