@@ -11,8 +11,9 @@ Inputs are seeded N(0,1) bf16 tensors already resident in HBM; the session is
 prefilled through frames 0..25 (untimed) and timed frames cycle through 8
 seeded frames' inputs while frame ids, slots and evictions advance normally.
 
-Prints one JSON line.  Kernel durations come from HIP events recorded on the
-stream the library launches on, around each call inside the timed region.
+Prints one JSON line.  `value` comes from the first timed region; per-kernel
+durations come from a second timed region of the same length in which the
+library brackets each kernel it launches with HIP events on this stream.
 The cpu_baseline leg times the fp64 oracle on a bounded sample (rank 0, N=1).
 """
 import argparse
@@ -59,7 +60,6 @@ def cpu_baseline(wl, target_s):
     for t in range(PREFILL):
         _, k, v = sf_inputs.frame_tensors(one, 0, 0, t)
         orc.step(t, {0: (sf_inputs.to_host_bytes(k), sf_inputs.to_host_bytes(v))})
-    frames = []
     t = PREFILL
     q, k, v = (sf_inputs.to_host_bytes(x) for x in sf_inputs.frame_tensors(one, 0, 0, t))
     start = time.perf_counter()
@@ -123,22 +123,13 @@ def main():
     qarr = [[(ctypes.c_void_p * 1)(p[0]) for p in frame] for frame in ring_ptrs]
     oarr = (ctypes.c_void_p * 1)(out.data_ptr())
 
-    def one_frame(t, ev=None):
-        i = (t - PREFILL) % RING
-        frame = ring_ptrs[i]
-        if ev is not None:
-            ev[0].record(stream)
+    def one_frame(t):
+        frame = ring_ptrs[(t - PREFILL) % RING]
         rc = lib.sf_evict(h, t, sptr)
-        if ev is not None:
-            ev[1].record(stream)
         for b in range(nb):
-            _, kp, vp = frame[b]
+            qp, kp, vp = frame[b]
             rc |= lib.sf_write_record(h, b, t, kp, vp, sptr)
-            if ev is not None:
-                ev[2 + 2 * b].record(stream)
-            rc |= lib.sf_attend(hs, 1, b, qarr[i][b], oarr, 0.0, sptr)
-            if ev is not None:
-                ev[3 + 2 * b].record(stream)
+            rc |= lib.sf_attend(hs, 1, b, qarr[(t - PREFILL) % RING][b], oarr, 0.0, sptr)
         if rc != 0:
             raise RuntimeError("libsf call failed: " + sf.sf_last_error(h))
 
@@ -149,33 +140,42 @@ def main():
     torch.cuda.synchronize()
     assert sess.view()["n_keys"] == 6528
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * nb)] for _ in range(args.steps)]
-    start_ev = torch.cuda.Event(enable_timing=True)
-    end_ev = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start_ev.record(stream)
-    for s_i in range(args.steps):
-        one_frame(t, events[s_i])
-        t += 1
-    end_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start_ev.elapsed_time(end_ev)
+    def timed(steps):
+        nonlocal t
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            one_frame(t)
+            t += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
 
-    attn_ms = [e[2 + 2 * b].elapsed_time(e[3 + 2 * b]) for e in events for b in range(nb)]
-    write_ms = [(e[1] if b == 0 else e[1 + 2 * b]).elapsed_time(e[2 + 2 * b]) for e in events for b in range(nb)]
-    evict_ms = [e[0].elapsed_time(e[1]) for e in events]
-    avg = lambda xs: sum(xs) / len(xs)
+    # Timed region 1: the step as a caller runs it (the value).
+    wall0 = time.perf_counter()
+    total_ms = timed(args.steps)
+    wall = time.perf_counter() - wall0
+    # Timed region 2: the same steps with the library's kernel tracing on (HIP events
+    # recorded on this stream around every kernel it launches).
+    sf.sf_profile_enable(h, True)
+    traced_ms = timed(args.steps)
+    kt = sf.sf_kernel_times_read(h)
+    sf.sf_profile_enable(h, False)
+
+    avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
     n_keys = 6528
     attn_flop = 4.0 * R * n_keys * H * D
-    attn_avg_s = avg(attn_ms) * 1e-3
-    attn_tflops = attn_flop / attn_avg_s / 1e12
+    attn_avg_ms = avg("attend")
+    comb_avg_ms = avg("combine")
+    attn_tflops = attn_flop / (attn_avg_ms * 1e-3) / 1e12
+    call_tflops = attn_flop / ((attn_avg_ms + comb_avg_ms) * 1e-3) / 1e12
     row_bytes = H * D * 2
     evict_bytes = nb * 2 * 2 * X * row_bytes   # K and V, read + write, every block
     write_bytes = 2 * 2 * R * row_bytes        # K and V, read + write, one block
-    evict_gbps = evict_bytes / (avg(evict_ms) * 1e-3) / 1e9
-    write_gbps = write_bytes / (avg(write_ms) * 1e-3) / 1e9
+    evict_gbps = evict_bytes / (avg("evict") * 1e-3) / 1e9
+    write_gbps = write_bytes / (avg("write") * 1e-3) / 1e9
     frames_per_s = args.steps / (total_ms * 1e-3)
 
     result = {
@@ -197,14 +197,19 @@ def main():
                    "blocks": nb, "heads": H, "head_dim": D, "record_rows": R, "keys": n_keys},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "sf_attend (attn_bf16_kernel<64> + split combine)",
-                     "flop_per_launch": attn_flop, "avg_launch_us": round(attn_avg_s * 1e6, 3)},
+                     "kernel": "attn_sk_kernel (head_dim 64 attention, stream-K)",
+                     "flop_per_launch": attn_flop, "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "launches": kt["attend"][1]},
         "attn_tflops": round(attn_tflops, 2),
+        "attend_call_tflops": round(call_tflops, 2),
+        "combine_avg_us": round(comb_avg_ms * 1e3, 3),
         "evict_gbps": round(evict_gbps, 1),
         "evict_frac_hbm": round(evict_gbps / PEAK_HBM_GBPS, 4),
-        "evict_avg_us": round(avg(evict_ms) * 1e3, 3),
+        "evict_avg_us": round(avg("evict") * 1e3, 3),
         "write_gbps": round(write_gbps, 1),
-        "write_avg_us": round(avg(write_ms) * 1e3, 3),
+        "write_frac_hbm": round(write_gbps / PEAK_HBM_GBPS, 4),
+        "write_avg_us": round(avg("write") * 1e3, 3),
+        "traced_ms_per_step": round(traced_ms / args.steps, 4),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -4,7 +4,7 @@ Thin ctypes marshalling over the C-ABI declared in include/sf.h: the functions
 here carry the C names and do no arithmetic of the method; every step runs in
 the library's gfx950 kernels.  Device memory and streams come from PyTorch
 (tensors' data pointers, torch.cuda streams).  Importing fails loudly when the
-library has not been built (python -m compressed_memory_kv_amd.build); there is
+library has not been built (python compressed_memory_kv_amd/build.py); there is
 no fallback path.
 
 Model card "GTA world model: weights and inference code", section "One buffer,
@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SF_LIB_PATH") or os.path.join(_HERE, "libsf.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m compressed_memory_kv_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python compressed_memory_kv_amd/build.py` "
                       "(the HIP library is the only implementation; there is no fallback)")
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -34,8 +34,10 @@ DTYPES = {"f32": SF_F32, "bf16": SF_BF16}
 EXPORTED = (
     "sf_config_check", "sf_buffer_bytes", "sf_kv_bytes", "sf_kv_offset", "sf_buffer_create",
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
-    "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch",
+    "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
 )
+SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_KINDS = 0, 1, 2, 3, 4, 5
+KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine")
 
 
 class sf_config(ctypes.Structure):
@@ -50,6 +52,10 @@ class sf_view(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("seg_begin", ctypes.c_int64 * SF_MAX_SEGMENTS),
                 ("seg_len", ctypes.c_int64 * SF_MAX_SEGMENTS), ("raw_frame", ctypes.POINTER(ctypes.c_int64)),
                 ("sum_frame", ctypes.POINTER(ctypes.c_int64))]
+
+
+class sf_kernel_times(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * SF_K_KINDS), ("launches", ctypes.c_int64 * SF_K_KINDS)]
 
 
 _P = ctypes.c_void_p
@@ -71,6 +77,8 @@ _sig = {
     "sf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sf_last_error": (ctypes.c_char_p, [_P]),
     "sf_debug_fail_next_launch": (ctypes.c_int, [_P]),
+    "sf_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "sf_kernel_times_read": (ctypes.c_int, [_P, ctypes.POINTER(sf_kernel_times)]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -209,6 +217,17 @@ def sf_last_error(handle: int | None = None) -> str:
 
 def sf_debug_fail_next_launch(handle: int) -> None:
     _check(_lib.sf_debug_fail_next_launch(handle), handle)
+
+
+def sf_profile_enable(handle: int, on: bool = True) -> None:
+    _check(_lib.sf_profile_enable(handle, 1 if on else 0), handle)
+
+
+def sf_kernel_times_read(handle: int) -> dict:
+    """{kind: (total ms, launches)} of the kernels launched since the last read (waits for them)."""
+    t = sf_kernel_times()
+    _check(_lib.sf_kernel_times_read(handle, ctypes.byref(t)), handle)
+    return {KERNEL_KINDS[k]: (t.ms[k], t.launches[k]) for k in range(SF_K_KINDS)}
 
 
 # ------------------------------------------------------- a session on torch

@@ -1,6 +1,7 @@
 """Builds libsf.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc.
 
-Usage: python -m compressed_memory_kv_amd.build  (or build() from Python).
+Usage: python compressed_memory_kv_amd/build.py  (by path: importing the package would
+load the library this builds), or __graft_entry__.build().
 Every HIP file is compiled for gfx950 only, with packed fp32 VALU ops turned
 off, then linked into compressed_memory_kv_amd/libsf.so next to this file.
 """

@@ -122,6 +122,36 @@ bool readable(const sf_config& c, const Geo& g, const Slots& s, Segs* out) {
 
 }  // namespace
 
+// Event pairs bracketing each launch while tracing is on.
+struct Tracer {
+  bool on = false;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> pending;  // (kind, (start, end))
+  std::vector<hipEvent_t> free_events;
+  hipEvent_t get() {
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    // Device-scope release: the event does not wait for a system-wide flush,
+    // so the pair brackets the kernel more tightly.
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventReleaseToDevice) != hipSuccess) return nullptr;
+    return e;
+  }
+  void clear() {
+    for (auto& p : pending) {
+      free_events.push_back(p.second.first);
+      free_events.push_back(p.second.second);
+    }
+    pending.clear();
+  }
+  ~Tracer() {
+    clear();
+    for (hipEvent_t e : free_events) (void)hipEventDestroy(e);
+  }
+};
+
 struct sf_buffer {
   sf_config cfg;
   Geo geo;
@@ -131,7 +161,38 @@ struct sf_buffer {
   std::vector<int64_t> written_at;  // per block: newest frame written, -1 none
   bool fail_next = false;
   std::string err;
+  Tracer trace;
 };
+
+namespace {
+
+// Brackets one launch with events when tracing is on.
+struct TraceScope {
+  Tracer& t;
+  int kind;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  TraceScope(Tracer& tr, int k, hipStream_t s) : t(tr), kind(k), st(s) {
+    if (!t.on) return;
+    a = t.get();
+    b = t.get();
+    if (a && b && hipEventRecord(a, st) == hipSuccess) return;
+    if (a) t.free_events.push_back(a);
+    if (b) t.free_events.push_back(b);
+    a = b = nullptr;
+  }
+  ~TraceScope() {
+    if (!t.on || !a || !b) return;
+    if (hipEventRecord(b, st) == hipSuccess) {
+      t.pending.push_back({kind, {a, b}});
+    } else {
+      t.free_events.push_back(a);
+      t.free_events.push_back(b);
+    }
+  }
+};
+
+}  // namespace
 
 namespace {
 
@@ -198,6 +259,7 @@ sf_status apply_evict(sf_buffer* b, int64_t t, const EvictPlan& p, hipStream_t s
     const int64_t row_bytes = b->geo.row_elems * eb;
     const int64_t src = (b->geo.R * (1 + p.s) + c.hw) * row_bytes;
     const int64_t dst = (b->geo.R * (c.y + 2) + (int64_t)p.u * c.x) * row_bytes;
+    TraceScope ts(b->trace, SF_K_EVICT, st);
     hipError_t e = sf::launch_evict(b->mem, c.n_blocks, (size_t)b->geo.block_stride, (size_t)b->geo.tensor_bytes,
                                     (size_t)src, (size_t)dst, (size_t)(c.x * row_bytes), st);
     if (e != hipSuccess) return hip_fail(b, e, "evict launch");
@@ -235,6 +297,7 @@ sf_status apply_write(sf_buffer* b, int32_t block, int64_t t, const void* k, con
   if (!b->dry) {
     char* kb = b->mem + block * b->geo.block_stride + row0 * row_bytes;
     char* vb = kb + b->geo.tensor_bytes;
+    TraceScope ts(b->trace, SF_K_WRITE, st);
     hipError_t e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
     if (e != hipSuccess) return hip_fail(b, e, "write launch");
   }
@@ -313,9 +376,16 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     if (G >= 8) G -= G % 8;
     a.n_wg = (int32_t)G;
     a.n_iters = (int32_t)iters;
-    hipError_t e = sf::launch_attend_sk(a, st);
+    hipError_t e;
+    {
+      TraceScope ts(b0->trace, SF_K_ATTEND, st);
+      e = sf::launch_attend_sk(a, st);
+    }
     if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
-    e = sf::launch_combine_sk(a, (int)units_total, st);
+    {
+      TraceScope ts(b0->trace, SF_K_COMBINE, st);
+      e = sf::launch_combine_sk(a, (int)units_total, st);
+    }
     if (e != hipSuccess) return hip_fail(b0, e, "combine launch");
   }
   return SF_OK;
@@ -388,9 +458,14 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     (void)base_units;
     if (units >= ((int64_t)1 << 30)) return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
     a.total_units = (int32_t)units;
-    hipError_t e = bf16 ? sf::launch_attend_bf16(a, st) : sf::launch_attend_f32(a, st);
+    hipError_t e;
+    {
+      TraceScope ts(b0->trace, SF_K_ATTEND, st);
+      e = bf16 ? sf::launch_attend_bf16(a, st) : sf::launch_attend_f32(a, st);
+    }
     if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
     if (bf16) {
+      TraceScope ts(b0->trace, SF_K_COMBINE, st);
       e = sf::launch_combine(a, st);
       if (e != hipSuccess) return hip_fail(b0, e, "combine launch");
     }
@@ -618,6 +693,39 @@ const char* sf_status_str(sf_status s) {
 }
 
 const char* sf_last_error(const sf_buffer* buf) { return buf ? buf->err.c_str() : g_thread_error.c_str(); }
+
+sf_status sf_profile_enable(sf_buffer* buf, int32_t on) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  if (buf->dry) return fail(buf, SF_E_STATE, "dry-run handles launch nothing to time");
+  if (!on) buf->trace.clear();
+  buf->trace.on = on != 0;
+  return SF_OK;
+}
+
+sf_status sf_kernel_times_read(sf_buffer* buf, sf_kernel_times* out) {
+  if (!buf || !out) return fail(buf, SF_E_ARG, "sf_kernel_times_read: NULL argument");
+  for (int k = 0; k < SF_K_KINDS; ++k) {
+    out->ms[k] = 0.0;
+    out->launches[k] = 0;
+  }
+  for (auto& p : buf->trace.pending) {
+    hipError_t e = hipEventSynchronize(p.second.second);
+    if (e != hipSuccess) {
+      buf->trace.clear();
+      return hip_fail(buf, e, "event wait");
+    }
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, p.second.first, p.second.second);
+    if (e != hipSuccess) {
+      buf->trace.clear();
+      return hip_fail(buf, e, "event elapsed time");
+    }
+    out->ms[p.first] += ms;
+    out->launches[p.first] += 1;
+  }
+  buf->trace.clear();
+  return SF_OK;
+}
 
 sf_status sf_debug_fail_next_launch(sf_buffer* buf) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");

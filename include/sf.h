@@ -173,6 +173,19 @@ const char* sf_last_error(const sf_buffer* buf);
 /* Test hook: the next device launch made through buf fails with SF_E_HIP before launching. */
 sf_status sf_debug_fail_next_launch(sf_buffer* buf);
 
+/* Kernel timing (tracing).  While enabled on a handle, every kernel the library launches
+ * for it is bracketed by two HIP events on the caller's stream.  sf_kernel_times waits for
+ * those events, returns the summed milliseconds and launch counts per kind since the last
+ * read, and starts a new period.  Kinds: */
+enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_KINDS = 5 };
+typedef struct sf_kernel_times {
+  double ms[SF_K_KINDS];
+  int64_t launches[SF_K_KINDS];
+} sf_kernel_times;
+/* on != 0 enables, 0 disables (pending events are dropped).  Dry-run handles: SF_E_STATE. */
+sf_status sf_profile_enable(sf_buffer* buf, int32_t on);
+sf_status sf_kernel_times_read(sf_buffer* buf, sf_kernel_times* out);
+
 #ifdef __cplusplus
 }
 #endif

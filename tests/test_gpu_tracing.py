@@ -1,0 +1,31 @@
+"""The library's kernel tracing: one event pair per launch, per kernel kind, on the caller's stream."""
+import pytest
+import torch
+
+import sf_inputs
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
+
+
+@needs_gpu
+def test_kernel_times_count_every_launch():
+    import compressed_memory_kv_amd as sf
+    wl = dict(sf_inputs.WORKLOADS["served1"], n_blocks=2)
+    sess = sf.Session(sf.make_config(**wl))
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    sf.sf_profile_enable(sess.handle, True)
+    frames = 6
+    for t in range(frames):
+        for b in range(2):
+            q, k, v = sf_inputs.frame_tensors(wl, 0, b, t, device="cuda")
+            sess.step(b, t, q, k, v, out)
+    times = sf.sf_kernel_times_read(sess.handle)
+    assert times["write"][1] == 2 * frames
+    assert times["attend"][1] == 2 * frames
+    assert times["combine"][1] == 2 * frames
+    assert times["evict"][1] == frames - 4          # at t = 4, 5 frames 1, 2 leave RAW (Y = 2)
+    assert all(times[k][0] > 0.0 for k in ("write", "attend", "combine", "evict"))
+    again = sf.sf_kernel_times_read(sess.handle)   # a read starts a new period
+    assert all(n == 0 for _, n in again.values())
+    sf.sf_profile_enable(sess.handle, False)

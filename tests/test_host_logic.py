@@ -244,3 +244,11 @@ def test_plan_properties(hw, x, y, extra, t):
     assert set(f for f in p["sum_frame"] if f >= 1) == set(range(max(1, t - w), t - y))
     if t >= w + 1:
         assert p["segments"] == [(0, C)]                           # steady state: one dense prefix
+
+
+def test_tracing_on_dry_handles():
+    s, wl = dry_session("tiny")
+    expect(sf.SF_E_STATE, sf.sf_profile_enable, s.handle, True)
+    times = sf.sf_kernel_times_read(s.handle)
+    assert all(ms == 0.0 and n == 0 for ms, n in times.values())
+    assert set(times) == set(sf.KERNEL_KINDS)
