@@ -34,6 +34,23 @@ PREFILL = 26                # frames 0..25: from frame 25 on, every read has the
 RING = 8
 
 
+def profiled_traffic(profile, source):
+    """HBM bytes per launch of a kernel from its committed counter summary, or None.
+
+    The summary records the sha256 of the kernel source it was measured on; a
+    kernel changed since then has no valid counter figure."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, profile)).read()
+        fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith(" "))
+        want = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != want:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,7 +213,9 @@ def main():
                                "(record write + attention)",
                    "blocks": nb, "heads": H, "head_dim": D, "record_rows": R, "keys": n_keys},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic("profiles/attn_sk_kernel.served_rollout.txt",
+                                                 "compressed_memory_kv_amd/csrc/sf_attn_sk.hip"),
                      "kernel": "attn_sk_kernel (head_dim 64 attention, stream-K)",
                      "flop_per_launch": attn_flop, "avg_launch_us": round(attn_avg_ms * 1e3, 3),
                      "launches": kt["attend"][1]},
