@@ -36,8 +36,8 @@ EXPORTED = (
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
 )
-SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_KINDS = 0, 1, 2, 3, 4, 5
-KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine")
+SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_KINDS = 0, 1, 2, 3, 4, 5, 6
+KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail")
 
 
 class sf_config(ctypes.Structure):

@@ -1,46 +1,54 @@
-// The dense read of the per-block memory, head_dim 64, as a persistent
+// The dense read of the per-block memory, head_dim 64, bf16, as a persistent
 // stream-K kernel for gfx950.
 //
 // Model card "GTA world model: weights and inference code", sections "What a
 // frame attends to" and "One buffer, no mask": every row of frame t's record
 // attends, with no mask, to every filled row of the block's K/V buffer:
 //     O[i,h] = sum_j softmax_j(scale * <Q[i,h], K[j,h]>) V[j,h]
-// The filled rows are at most a few contiguous segments; the kernel walks them
+// The filled rows are at most a few contiguous segments; the kernels walk them
 // as one flattened key sequence (addressing, not masking).
 //
-// Work decomposition.  A unit is (session, head, 128-row query tile); its work
-// is ceil(keys/64) iterations of 64 keys.  The iterations of all units of the
-// launch, in order, are cut into G equal contiguous ranges, one per persistent
-// workgroup (G = number of CUs, one 8-wave workgroup per CU).  Consecutive
-// ranges share a head, and the grid is remapped so each XCD (the hardware deals
-// workgroups round robin over the 8 XCDs) owns a contiguous eighth: a head's K/V
-// stays in one XCD's L2.  The part of a unit inside one workgroup's range is a
-// "piece".  A piece that is the whole unit writes the output; otherwise it
-// writes an unnormalised partial (O, reference max, row sum) to the session's
-// scratch and combine_sk_kernel merges the pieces of the unit.
+// Work decomposition.  A unit is (session, head, 128-row query tile).  Its keys
+// are floor(keys/64) full 64-key tiles plus, when keys is not a multiple of 64,
+// a tail of fewer than 64 keys.
+//   attn_sk_kernel: the full tiles of all units of the launch, in order, are cut
+//     into G equal contiguous ranges, one per persistent workgroup (G = number of
+//     CUs, one 8-wave workgroup per CU).  Consecutive ranges share a head, and the
+//     grid is remapped so each XCD (the hardware deals workgroups round robin over
+//     the 8 XCDs) owns a contiguous eighth: a head's K/V stays in one XCD's L2.
+//     The part of a unit inside one workgroup's range is a "piece"; a piece that is
+//     the whole unit (and the unit has no tail) writes the output, otherwise it
+//     writes an unnormalised partial (O, reference max, row sum) to the session's
+//     scratch;
+//   attn_tail_kernel: one workgroup per unit with a tail writes the tail's
+//     partial to the unit's last scratch slot;
+//   combine_sk_kernel: merges the partials of every unit that has more than one.
 //
-// Inside a workgroup.  Eight waves = four key streams x two waves.  The piece's
-// tiles are cut into four contiguous quarters, one per stream; the two waves of
-// a stream hold 64 query rows each (two 32-row MFMA blocks), so every K/V
-// operand read from LDS feeds two MFMAs.  Per stream, K and V tiles go from
-// global memory straight into LDS (global_load_lds_dwordx4: no staging VGPRs)
-// into two stages, kept as two separate LDS arrays so the compiler can tell the
-// tile in flight from the tile being read; the next tile's transfer overlaps
-// the current tile's compute and the barrier ending each step waits for it.
-// At the end of a piece the four streams are merged through LDS.
+// Inside a workgroup of attn_sk_kernel.  Eight waves = four key streams x two
+// waves; the piece's tiles are cut into four contiguous quarters, one per
+// stream.  The two waves of a stream hold 64 query rows each (two 32-row MFMA
+// blocks), so every K/V operand read from LDS feeds two MFMAs.  K and V tiles go
+// from global memory straight into LDS (global_load_lds_dwordx4, no staging
+// VGPRs), double buffered.
 //
-// Per tile and wave, in two halves of 32 keys:
-//   S^T (32 keys x 32 queries, per query block) = K . Q^T on
-//     v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q in VGPRs), so each
-//     lane owns one query and 16 of its scores;
-//   P = exp2(S * scale*log2e - mref) in fp32, rounded to bf16, and its row sum
-//     taken from the rounded values (v_dot2_f32_bf16 against ones).  The
-//     reference mref moves only when some p of the half would exceed 2^15 (a
-//     wave-uniform test on the sums) and on a stream's first half-tile: then
-//     the true max of the half is taken and O and the sum are rescaled.  Exact
-//     softmax either way, up to rounding;
-//   O^T (64 x 32 queries, per query block) += V^T . P^T on the same MFMA; V^T
-//     comes from the row-major V tile through ds_read_b64_tr_b16.
+// Softmax with a fixed reference.  Each stream takes one reference per query,
+// the max of its first tile's scores, and keeps it: p = exp2(s*c - mref) may
+// exceed 1 but no rescaling of O is ever needed inside the loop, which is
+// therefore branch-free.  A lane's largest quarter sum is tracked; if in some
+// stream of the workgroup a p could have exceeded 2^40 (or overflowed), the
+// workgroup redoes the piece with the exact max over each stream's keys, where
+// every p is at most 1.  Exact softmax either way, up to rounding.
+//
+// Per 64-key tile and wave: four "quarters" (32-key half h, 32-query block qb),
+//   S^T (32 keys x 32 queries) = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows
+//     from LDS, B = Q in VGPRs): each lane owns one query and 16 of its scores;
+//   P = exp2(S * scale*log2e - mref) in fp32, rounded to bf16 (nearest even); the
+//     row sum adds the fp32 values;
+//   O^T (64 x 32 queries) += V^T . P^T on the same MFMA; V^T comes from the
+//     row-major V tile through ds_read_b64_tr_b16.
+// The quarters are software pipelined across tiles: in each region the matrix
+// core computes one quarter's S^T and an earlier quarter's O^T while the VALU does
+// the softmax of a quarter whose S^T is already there.
 #include "sf_internal.h"
 
 #include <cmath>
@@ -49,30 +57,29 @@ namespace sf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int D = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStreams = 4;
-constexpr int kStreamThreads = kThreads / kStreams;  // 128
-constexpr int BN = kSkKeys;
+constexpr int BN = kSkKeys;                           // 64 keys per tile
 constexpr int ROW = 2 * D;                            // bytes per K/V row
 constexpr int TILE = BN * ROW;                        // 8 KB
 constexpr int STAGE = 2 * TILE;                       // K tile then V tile
-constexpr int STAGE_ALL = kStreams * STAGE;          // one stage of every stream (64 KB)
+constexpr int STAGE_ALL = kStreams * STAGE;           // one stage of every stream (64 KB)
 constexpr int DMA_ROWS = 8;                           // rows one wave-wide 1 KB transfer covers
 constexpr int DMA_PER_WAVE = BN / DMA_ROWS / 2;       // transfers per wave per tensor per tile (4)
-constexpr float kSumLimit = 32768.0f;
+constexpr float kOverflowSum = 0x1p40f;               // a lane quarter sum above this asks for exact maxima
 // Stream merge buffer: 3 streams x 2 waves x 64 lanes x (64 O + 2 m + 2 l) floats,
 // slots 0-2 in stage array a, 3-5 in stage array b.
 constexpr int MERGE_FLOATS = 68;
 constexpr int MERGE_SLOT = 64 * MERGE_FLOATS * 4;
 static_assert(3 * MERGE_SLOT <= STAGE_ALL, "three merge slots fit in one stage array");
+static_assert(BN == 64, "a tile is two 32-key MFMA blocks");
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
@@ -89,11 +96,85 @@ __device__ __forceinline__ int session_of_iter(const SkLaunch& a, int it) {
   return __builtin_amdgcn_readfirstlane(si);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// Session and unit of a unit index counted over the whole launch.
+__device__ __forceinline__ void decode_unit(const SkLaunch& a, int ug, int& si, int& u) {
+  int s = 0, base = 0, acc = 0;
+  for (int i = 0; i < a.n_sessions; ++i) {
+    if (ug >= acc) {
+      s = i;
+      base = acc;
+    }
+    acc += a.n_heads * a.s[i].qtiles;
+  }
+  si = __builtin_amdgcn_readfirstlane(s);
+  u = __builtin_amdgcn_readfirstlane(ug - base);
+}
+
+// Buffer row of flattened key kappa (segments in ascending key order).
+__device__ __forceinline__ int key_row(const int* seg_row, const int* seg_key, int kappa) {
+  int row = seg_row[0] + kappa;
+#pragma unroll
+  for (int i = 1; i < SF_MAX_SEGMENTS; ++i) row = kappa >= seg_key[i] ? seg_row[i] + (kappa - seg_key[i]) : row;
+  return row;
+}
+
+__device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int* seg_key) {
+  int cum = 0;
+#pragma unroll
+  for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
+    const bool used = i < S.n_seg;
+    seg_row[i] = used ? S.seg_begin[i] : 0;
+    seg_key[i] = used ? cum : 0x7fffffff;
+    cum += used ? S.seg_len[i] : 0;
+  }
+}
+
+// ---- MFMA building blocks shared by both attention kernels ---------------------------
+// S^T of a quarter: 4 MFMA over the head dimension (A = K rows from LDS, B = Q^T).
+#define SK_QK(SD, KOP, QOP)                                                               \
+  SD = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KOP[0], QOP[0], zero16, 0, 0, 0);          \
+  SD = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KOP[1], QOP[1], SD, 0, 0, 0);              \
+  SD = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KOP[2], QOP[2], SD, 0, 0, 0);              \
+  SD = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KOP[3], QOP[3], SD, 0, 0, 0);
+// O^T += V^T . P^T of a quarter: 2 key steps of 16 x 2 d blocks.
+#define SK_PV(O0, O1, VOP, P)                                                             \
+  O0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VOP[0], P[0], O0, 0, 0, 0);                \
+  O1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VOP[1], P[0], O1, 0, 0, 0);                \
+  O0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VOP[2], P[1], O0, 0, 0, 0);                \
+  O1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VOP[3], P[1], O1, 0, 0, 0);
+// LDS operands of 32 keys starting at row R0 of a stage: K rows (A of S^T) and V^T
+// (A of O^T; entry 2*j + db for key step j and d block db).
+#define SK_LOAD_K(KOP, ST, R0)                                                            \
+  _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KOP[kk] =                              \
+      *reinterpret_cast<const bf16x8*>((ST) + kaddr[kk] + (R0) * ROW);
+#define SK_LOAD_V(VOP, ST, R0)                                                            \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
+    _Pragma("unroll") for (int db = 0; db < 2; ++db) {                                    \
+      const char* vp_ = (ST) + vaddr[db] + ((R0) + 16 * j) * ROW;                         \
+      const i16x4 va_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp_));       \
+      const i16x4 vb_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp_ + 8 * ROW)); \
+      VOP[2 * j + db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va_, vb_, 0, 1, 2, 3, 4, 5, 6, 7)); \
+    }                                                                                     \
+  }
+// Lane addresses of those operands inside a stage (K chunk c of row r at c ^ (r & 7),
+// V chunk c at c ^ 2*(r & 3): conflict-free reads).
+#define SK_OPERAND_ADDRESSES(BASE)                                                        \
+  int kaddr[4];                                                                           \
+  _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) kaddr[kk] =                            \
+      (BASE) + l32 * ROW + (((2 * kk + g) ^ (l32 & 7)) << 4);                             \
+  int vaddr[2];                                                                           \
+  {                                                                                       \
+    const int trow_ = (lane >> 2) & 3;                                                    \
+    _Pragma("unroll") for (int db = 0; db < 2; ++db) {                                    \
+      const int chunk_ = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);              \
+      vaddr[db] = (BASE) + TILE + (4 * g + trow_) * ROW + ((chunk_ ^ (2 * trow_)) << 4) + 8 * (lane & 1); \
+    }                                                                                     \
+  }
 
 __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
+  __shared__ int redo[kWaves];
   const int G = a.n_wg;
   const int N = a.n_iters;
   const int w = (G & 7) == 0 ? (int)(blockIdx.x & 7u) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
@@ -111,26 +192,16 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   const int l32 = lane & 31;
   const int soff = stream * STAGE;  // this stream's stage within a stage array
 
-  // Stage layout (as in sf_attn.hip): K chunk c of row r sits at c ^ (r & 7), V chunk c
-  // at c ^ 2*(r & 3).  A wave-wide transfer fills 1 KB = 8 rows, lane L landing at
-  // row L/8, position L%8, so lane L fetches the logical chunk that belongs there
-  // (both swizzles are involutions).  Rows of a tile differ by multiples of 8 between
-  // a wave's transfers, so the chunk a lane fetches is the same for all of them.
-  const int drow = lane >> 3;                                  // row within a transfer
-  const int kchunk = (lane & 7) ^ drow;                        // K: p ^ (r & 7)
-  const int vchunk = (lane & 7) ^ (2 * (drow & 3));            // V: p ^ 2*(r & 3)
-  const int trow0 = hw * DMA_PER_WAVE * DMA_ROWS + drow;       // tile row of transfer 0
-  int kaddr[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kaddr[kk] = l32 * ROW + (((2 * kk + g) ^ (l32 & 7)) << 4);
-  const int trow = (lane >> 2) & 3;
-  int vaddr[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    vaddr[db] = TILE + (4 * g + trow) * ROW + ((chunk ^ (2 * trow)) << 4) + 8 * (lane & 1);
-  }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // A wave-wide transfer fills 1 KB = 8 rows of a stage, lane L landing at row L/8,
+  // position L%8, so lane L fetches the logical chunk that belongs there (both
+  // swizzles are involutions; transfers start at multiples of 8 rows, so the chunk a
+  // lane fetches is the same for all of them).  Each wave moves its 32-row half.
+  const int drow = lane >> 3;
+  const int kchunk = (lane & 7) ^ drow;
+  const int vchunk = (lane & 7) ^ (2 * (drow & 3));
+  const int trow0 = hw * DMA_PER_WAVE * DMA_ROWS + drow;  // tile row of transfer 0
+  SK_OPERAND_ADDRESSES(soff);
+  const f32x16 zero16 = {};
 
   for (int it = it_lo; it < it_hi;) {
     // ---- the piece: one unit's tiles [tile0, tile1) inside this workgroup's range
@@ -143,9 +214,8 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     const int tile1 = min(nt, tile0 + (it_hi - it));
     const int qt = __builtin_amdgcn_readfirstlane(u % S.qtiles);
     const int h = __builtin_amdgcn_readfirstlane(u / S.qtiles);
-    const int key_hi = min(tile1 * BN, S.n_keys);
     const int n = tile1 - tile0;
-    const int s_lo = tile0 + (stream * n) / kStreams;
+    const int s_lo = tile0 + (stream * n) / kStreams;   // this stream's tiles [s_lo, s_hi)
     const int s_hi = tile0 + ((stream + 1) * n) / kStreams;
     const int steps = (n + kStreams - 1) / kStreams;
     const int row_stride = H * D;
@@ -154,35 +224,28 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     const bool wave_on = qrow0 < S.rows;
 
     int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
-    {
-      int cum = 0;
-#pragma unroll
-      for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
-        const bool used = i < S.n_seg;
-        seg_row[i] = used ? S.seg_begin[i] : 0;
-        seg_key[i] = used ? cum : 0x7fffffff;
-        cum += used ? S.seg_len[i] : 0;
-      }
-    }
+    seg_tables(S, seg_row, seg_key);
 
     // Q^T operands: query block qb holds rows qrow0 + 32*qb + l32 (rows past R read row R-1).
-    bf16x8 qreg[2][4];
+    bf16x8 q0[4], q1[4];
+    {
+      const int r0 = min(qrow0 + l32, S.rows - 1);
+      const int r1 = min(qrow0 + 32 + l32, S.rows - 1);
+      const __bf16* qp0 = reinterpret_cast<const __bf16*>(S.q) + r0 * row_stride + h * D + 8 * g;
+      const __bf16* qp1 = reinterpret_cast<const __bf16*>(S.q) + r1 * row_stride + h * D + 8 * g;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int row = min(qrow0 + 32 * qb + l32, S.rows - 1);
-      const __bf16* qp = reinterpret_cast<const __bf16*>(S.q) + row * row_stride + h * D + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qreg[qb][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        q0[kk] = *reinterpret_cast<const bf16x8*>(qp0 + 16 * kk);
+        q1[kk] = *reinterpret_cast<const bf16x8*>(qp1 + 16 * kk);
+      }
     }
 
     const char* __restrict__ kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
     const char* __restrict__ vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
 
     // Starts the transfer of this stream's tile TL into stage array ST (this wave's
-    // half: rows [32*hw, 32*hw+32) of K and of V).  A tile inside one segment is a
-    // run of rows (scalar base + fixed lane offsets); otherwise rows are looked up
-    // per lane, and keys past the piece's range re-read its last key (finite data
-    // that gets score -inf).
+    // half: rows [32*hw, 32*hw+32) of K and of V).  A tile inside one segment is a run
+    // of rows (scalar base + fixed lane offsets); otherwise rows are looked up per lane.
     auto dma_tile = [&](const int tl, char* st) {
       const int kap0 = tl * BN;
       int srow = seg_row[0], skey = seg_key[0], send = seg_key[1];
@@ -195,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       }
       char* kdst = st + soff + (trow0 - drow) * ROW;
       char* vdst = kdst + TILE;
-      if (kap0 + BN <= min(send, key_hi)) {
+      if (kap0 + BN <= send) {
         const unsigned base = (unsigned)((srow + kap0 - skey + trow0) * row_bytes);
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
@@ -206,126 +269,177 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       } else {
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
-          const int kappa = min(kap0 + trow0 + m * DMA_ROWS, key_hi - 1);
-          int row = seg_row[0] + kappa;
-#pragma unroll
-          for (int i = 1; i < SF_MAX_SEGMENTS; ++i)
-            row = kappa >= seg_key[i] ? seg_row[i] + (kappa - seg_key[i]) : row;
-          const unsigned rb = (unsigned)(row * row_bytes);
+          const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * DMA_ROWS) * row_bytes);
           __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
         }
       }
     };
 
-    f32x16 o[2][2];  // [d block][query block]
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][qb][r] = 0.0f;
-    float mref[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.0f, 0.0f};
+    f32x16 o00, o10, o01, o11;  // O^T blocks [d block][query block]
+    float mref0, mref1, lsum0, lsum1, tsmax;
 
-    // One 64-key tile of this stream from stage array STA.
-    auto compute_tile = [&](const int tl, const char* sta) {
-      const char* st = sta + soff;
+    // P = exp2(S*c - mref) rounded to bf16; the lane's sum of the fp32 values goes to the
+    // row sum, and the largest such sum is kept to detect a reference that is too low.
+#define SK_SOFTMAX(S, MREF, LSUM, P)                                                      \
+  {                                                                                       \
+    float h_[2];                                                                          \
+    _Pragma("unroll") for (int b_ = 0; b_ < 2; ++b_) {                                    \
+      float e_[8];                                                                        \
+      _Pragma("unroll") for (int r = 0; r < 8; ++r)                                       \
+          e_[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * b_ + r], c, -(MREF)));      \
+      _Pragma("unroll") for (int r = 0; r < 8; ++r) P[b_][r] = (__bf16)e_[r];             \
+      h_[b_] = ((e_[0] + e_[1]) + (e_[2] + e_[3])) + ((e_[4] + e_[5]) + (e_[6] + e_[7]));  \
+    }                                                                                     \
+    const float ts_ = h_[0] + h_[1];                                                      \
+    LSUM += ts_;                                                                          \
+    tsmax = fmaxf(tsmax, ts_);                                                            \
+  }
+    // Scheduling hints for one region: ND LDS reads first, NV0 VALU ops, then NM MFMAs
+    // each followed by NV VALU ops; the region ends there.
+#define SK_REGION_HINTS(ND, NV0, NM, NV)                                                  \
+  __builtin_amdgcn_sched_group_barrier(0x100, (ND), 0);                                   \
+  __builtin_amdgcn_sched_group_barrier(0x002, (NV0), 0);                                  \
+  _Pragma("unroll") for (int k_ = 0; k_ < (NM); ++k_) {                                   \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    \
+    __builtin_amdgcn_sched_group_barrier(0x002, (NV), 0);                                 \
+  }                                                                                       \
+  __builtin_amdgcn_sched_barrier(0);
+
+    // Pipeline over full tiles.  Quarters q0 = (h0, qb0), q1 = (h0, qb1), q2 = (h1, qb0),
+    // q3 = (h1, qb1).  State carried between steps: K(t) half 0 (kop0), V(t-1) half 1
+    // (vop1), S(t, q0) (sa) and P(t-1, q3) (p3).  Per step, tile t in CUR, tile t+1
+    // landing in NXT:
+    //   A: S(t,q1)    O(t-1,q3) | P(t,q0)
+    //   B: S(t,q2)    O(t,q0)   | P(t,q1)
+    //   C: S(t,q3)    O(t,q1)   | P(t,q2)
+    //   -- barrier: tile t+1 is in NXT for every wave --
+    //   D: S(t+1,q0)  O(t,q2)   | P(t,q3)
+    //   -- barrier: every wave is done with CUR, which the next step refills --
+    bf16x8 kop0[4], vop1[4], p2[2], p3[2];
+    f32x16 sa, sb;
+#define SK_STEP_ABC(CUR)                                                                  \
+  {                                                                                       \
+    bf16x8 kop1[4], vop0[4], p0[2], p1[2];                                                \
+    SK_QK(sb, kop0, q1);                                                                  \
+    SK_PV(o01, o11, vop1, p3);                                                            \
+    SK_SOFTMAX(sa, mref0, lsum0, p0);                                                     \
+    SK_REGION_HINTS(0, 0, 8, 7);                                                          \
+    SK_LOAD_K(kop1, CUR, 32);                                                             \
+    SK_LOAD_V(vop0, CUR, 0);                                                              \
+    SK_QK(sa, kop1, q0);                                                                  \
+    SK_PV(o00, o10, vop0, p0);                                                            \
+    SK_SOFTMAX(sb, mref1, lsum1, p1);                                                     \
+    SK_REGION_HINTS(12, 16, 8, 5);                                                        \
+    SK_QK(sb, kop1, q1);                                                                  \
+    SK_PV(o01, o11, vop0, p1);                                                            \
+    SK_SOFTMAX(sa, mref0, lsum0, p2);                                                     \
+    SK_REGION_HINTS(0, 0, 8, 7);                                                          \
+    SK_LOAD_V(vop1, CUR, 32);                                                             \
+  }
+#define SK_STEP_D(NXT)                                                                    \
+  {                                                                                       \
+    SK_LOAD_K(kop0, NXT, 0);                                                              \
+    SK_QK(sa, kop0, q0);                                                                  \
+    SK_PV(o00, o10, vop1, p2);                                                            \
+    SK_SOFTMAX(sb, mref1, lsum1, p3);                                                     \
+    SK_REGION_HINTS(4, 16, 8, 5);                                                         \
+  }
+
+    // Per-lane max of the raw scores of a tile in stage ST, both query blocks.
+    auto tile_max = [&](const char* st, float& mt0, float& mt1) {
+#pragma unroll 1
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 kop[4];
+        f32x16 s0, s1;
+        SK_LOAD_K(kop, st, 32 * hh);
+        SK_QK(s0, kop, q0);
+        SK_QK(s1, kop, q1);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        // S^T for keys 32*kh .. 32*kh+31 of the tile, both query blocks
-        f32x16 s[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { s[0][r] = 0.0f; s[1][r] = 0.0f; }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(st + kaddr[kk] + kh * 32 * ROW);
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[0][kk], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[1][kk], s[1], 0, 0, 0);
-        }
-        if (tl * BN + 32 * kh + 32 > key_hi) {  // ragged end of the piece
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = tl * BN + 32 * kh + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= key_hi) { s[0][r] = -INFINITY; s[1][r] = -INFINITY; }
-          }
-        }
-        bf16x8 pb[2][2];
-        float ts[2];
-        auto probs = [&]() {
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              pb[qb][0][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, -mref[qb]));
-              pb[qb][1][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 + r], c, -mref[qb]));
-            }
-            float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bf16x2 a0 = {pb[qb][0][2 * e], pb[qb][0][2 * e + 1]};
-              const bf16x2 a1 = {pb[qb][1][2 * e], pb[qb][1][2 * e + 1]};
-              p0 = __builtin_amdgcn_fdot2_f32_bf16(a0, ones, p0, false);
-              p1 = __builtin_amdgcn_fdot2_f32_bf16(a1, ones, p1, false);
-            }
-            ts[qb] = p0 + p1;
-          }
-        };
-        probs();
-        // The first half-tile of a stream always sets the reference (it is -inf before,
-        // so masked keys there give NaN p, which this path discards).  Later sums are
-        // finite or +inf, never NaN.
-        const bool first = tl == s_lo && kh == 0;
-        if (first || __any(ts[0] > kSumLimit || ts[1] > kSumLimit)) {
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            float mt = fmaxf(s[qb][0], s[qb][1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) mt = max3(mt, s[qb][r], s[qb][r + 1]);
-            mt = fmaxf(mt, xor32(mt)) * c;
-            const float mnew = fmaxf(mref[qb], mt);
-            const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
-            lsum[qb] *= alpha;
-            mref[qb] = mnew;
-          }
-          probs();
-        }
-        lsum[0] += ts[0];
-        lsum[1] += ts[1];
-        // O^T += V^T . P^T over this half's two 16-key k-steps
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int roff = (32 * kh + 16 * j) * ROW;
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff));
-            const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff + 8 * ROW));
-            const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[0][j], o[db][0], 0, 0, 0);
-            o[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[1][j], o[db][1], 0, 0, 0);
-          }
+        for (int r = 0; r < 16; r += 2) {
+          mt0 = max3(mt0, s0[r], s0[r + 1]);
+          mt1 = max3(mt1, s1[r], s1[r + 1]);
         }
       }
     };
 
-    // ---- pipeline over this stream's tiles [s_lo, s_hi): all waves take `steps` steps.
-    // Each step computes one stage while the next tile flows into the other; the
-    // barrier that ends the step also waits for that transfer.
-    if (s_lo < s_hi) dma_tile(s_lo, st_a);
-    __syncthreads();
-    for (int i = 0; i < steps; i += 2) {
-      const int tl = s_lo + i;
-      if (tl + 1 < s_hi) dma_tile(tl + 1, st_b);
-      if (tl < s_hi && wave_on) compute_tile(tl, st_a);
+    // Softmax with a reference fixed per query for the whole piece.  Attempt 0 takes the
+    // max of the stream's first tile; if some p could then have exceeded 2^40 (a lane's
+    // quarter sum above it, +inf included) anywhere in the workgroup, attempt 1 redoes the
+    // piece with the exact max over each stream's keys, where every p is at most 1.
+    for (int attempt = 0;; ++attempt) {
+      float mt0 = -INFINITY, mt1 = -INFINITY;
+      if (attempt == 0) {
+        if (s_lo < s_hi) dma_tile(s_lo, st_a);
+        __syncthreads();
+        if (s_lo < s_hi && wave_on) tile_max(st_a, mt0, mt1);
+        __syncthreads();
+      } else {
+        if (s_lo < s_hi) dma_tile(s_lo, st_a);
+        __syncthreads();
+        for (int i = 0; i < steps; i += 2) {
+          const int tl = s_lo + i;
+          if (tl + 1 < s_hi) dma_tile(tl + 1, st_b);
+          if (tl < s_hi && wave_on) tile_max(st_a, mt0, mt1);
+          __syncthreads();
+          if (i + 1 >= steps) break;
+          if (tl + 2 < s_hi) dma_tile(tl + 2, st_a);
+          if (tl + 1 < s_hi && wave_on) tile_max(st_b, mt0, mt1);
+          __syncthreads();
+        }
+        if (s_lo < s_hi) dma_tile(s_lo, st_a);  // the main loop starts from stage a
+        __syncthreads();
+      }
+      mref0 = fmaxf(mt0, xor32(mt0)) * c;
+      mref1 = fmaxf(mt1, xor32(mt1)) * c;
+      o00 = zero16;
+      o10 = zero16;
+      o01 = zero16;
+      o11 = zero16;
+      lsum0 = lsum1 = 0.0f;
+      tsmax = 0.0f;
+
+      // All waves take `steps` steps (uniform barriers); a wave whose stream has no tile
+      // at a step only takes part in the barriers.  The stream's first tile is in stage a.
+      const bool run = s_lo < s_hi && wave_on;
+      if (run) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vop1[q][e] = (__bf16)0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p3[0][e] = (__bf16)0.0f;
+          p3[1][e] = (__bf16)0.0f;
+        }
+        SK_LOAD_K(kop0, st_a, 0);
+        SK_QK(sa, kop0, q0);
+      }
+      for (int i = 0; i < steps; i += 2) {
+        const int tl = s_lo + i;
+        if (tl + 1 < s_hi) dma_tile(tl + 1, st_b);
+        if (tl < s_hi && wave_on) SK_STEP_ABC(st_a);
+        __syncthreads();
+        if (tl < s_hi && wave_on) SK_STEP_D(st_b);
+        __syncthreads();
+        if (i + 1 >= steps) break;
+        if (tl + 2 < s_hi) dma_tile(tl + 2, st_a);
+        if (tl + 1 < s_hi && wave_on) SK_STEP_ABC(st_b);
+        __syncthreads();
+        if (tl + 1 < s_hi && wave_on) SK_STEP_D(st_a);
+        __syncthreads();
+      }
+      if (run) SK_PV(o01, o11, vop1, p3);  // the stream's last quarter
+
+      // Workgroup-wide decision: redo the piece with exact maxima?
+      const int bad = __any(tsmax > kOverflowSum) ? 1 : 0;
+      if (lane == 0) redo[wave] = bad;
       __syncthreads();
-      if (i + 1 >= steps) break;
-      if (tl + 2 < s_hi) dma_tile(tl + 2, st_a);
-      if (tl + 1 < s_hi && wave_on) compute_tile(tl + 1, st_b);
+      int any_bad = 0;
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) any_bad |= redo[wv];
       __syncthreads();
+      if (!__builtin_amdgcn_readfirstlane(any_bad) || attempt == 1) break;
     }
 
     // ---- merge the four streams (stream 0 collects), then write
@@ -335,83 +449,85 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     if (stream > 0 && wave_on) {
       float* dst = merge_slot((stream - 1) * 2 + hw);
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 4)
-            *reinterpret_cast<float4*>(dst + (db * 2 + qb) * 16 + r) =
-                make_float4(o[db][qb][r], o[db][qb][r + 1], o[db][qb][r + 2], o[db][qb][r + 3]);
-      *reinterpret_cast<float4*>(dst + 64) = make_float4(mref[0], mref[1], lsum[0], lsum[1]);
+      for (int r = 0; r < 16; r += 4) {
+        *reinterpret_cast<float4*>(dst + 0 * 16 + r) = make_float4(o00[r], o00[r + 1], o00[r + 2], o00[r + 3]);
+        *reinterpret_cast<float4*>(dst + 1 * 16 + r) = make_float4(o01[r], o01[r + 1], o01[r + 2], o01[r + 3]);
+        *reinterpret_cast<float4*>(dst + 2 * 16 + r) = make_float4(o10[r], o10[r + 1], o10[r + 2], o10[r + 3]);
+        *reinterpret_cast<float4*>(dst + 3 * 16 + r) = make_float4(o11[r], o11[r + 1], o11[r + 2], o11[r + 3]);
+      }
+      *reinterpret_cast<float4*>(dst + 64) = make_float4(mref0, mref1, lsum0, lsum1);
     }
     __syncthreads();
     if (stream == 0 && wave_on) {
-      float mx[2] = {mref[0], mref[1]};
+      float mx0 = mref0, mx1 = mref1;
 #pragma unroll
       for (int s2 = 0; s2 < 3; ++s2) {
         const float4 ml = *reinterpret_cast<const float4*>(merge_slot(s2 * 2 + hw) + 64);
-        mx[0] = fmaxf(mx[0], ml.x);
-        mx[1] = fmaxf(mx[1], ml.y);
+        mx0 = fmaxf(mx0, ml.x);
+        mx1 = fmaxf(mx1, ml.y);
       }
-      float sc0[2] = {__builtin_amdgcn_exp2f(mref[0] - mx[0]), __builtin_amdgcn_exp2f(mref[1] - mx[1])};
-      float l[2] = {lsum[0] * sc0[0], lsum[1] * sc0[1]};
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][qb][r] *= sc0[qb];
+      // a stream without tiles has reference -inf and contributes nothing
+      const float f00 = __builtin_amdgcn_exp2f(mref0 - mx0), f01 = __builtin_amdgcn_exp2f(mref1 - mx1);
+      float l0 = lsum0 * f00, l1 = lsum1 * f01;
+      o00 *= f00;
+      o10 *= f00;
+      o01 *= f01;
+      o11 *= f01;
 #pragma unroll 1
       for (int s2 = 0; s2 < 3; ++s2) {  // one stream at a time keeps the live set small
         const float* src = merge_slot(s2 * 2 + hw);
         const float4 ml = *reinterpret_cast<const float4*>(src + 64);
-        const float f0 = __builtin_amdgcn_exp2f(ml.x - mx[0]);
-        const float f1 = __builtin_amdgcn_exp2f(ml.y - mx[1]);
-        l[0] += ml.z * f0;
-        l[1] += ml.w * f1;
+        const float f0 = __builtin_amdgcn_exp2f(ml.x - mx0);
+        const float f1 = __builtin_amdgcn_exp2f(ml.y - mx1);
+        l0 += ml.z * f0;
+        l1 += ml.w * f1;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-              const float4 x = *reinterpret_cast<const float4*>(src + (db * 2 + qb) * 16 + r);
-              const float f = qb == 0 ? f0 : f1;
-              o[db][qb][r] += f * x.x;
-              o[db][qb][r + 1] += f * x.y;
-              o[db][qb][r + 2] += f * x.z;
-              o[db][qb][r + 3] += f * x.w;
-            }
+        for (int r = 0; r < 16; r += 4) {
+          const float4 x00 = *reinterpret_cast<const float4*>(src + 0 * 16 + r);
+          const float4 x01 = *reinterpret_cast<const float4*>(src + 1 * 16 + r);
+          const float4 x10 = *reinterpret_cast<const float4*>(src + 2 * 16 + r);
+          const float4 x11 = *reinterpret_cast<const float4*>(src + 3 * 16 + r);
+          o00[r] += f0 * x00.x; o00[r + 1] += f0 * x00.y; o00[r + 2] += f0 * x00.z; o00[r + 3] += f0 * x00.w;
+          o01[r] += f1 * x01.x; o01[r + 1] += f1 * x01.y; o01[r + 2] += f1 * x01.z; o01[r + 3] += f1 * x01.w;
+          o10[r] += f0 * x10.x; o10[r + 1] += f0 * x10.y; o10[r + 2] += f0 * x10.z; o10[r + 3] += f0 * x10.w;
+          o11[r] += f1 * x11.x; o11[r + 1] += f1 * x11.y; o11[r + 2] += f1 * x11.z; o11[r + 3] += f1 * x11.w;
+        }
       }
-      const float lt[2] = {l[0] + xor32(l[0]), l[1] + xor32(l[1])};
-      const bool whole = tile0 == 0 && tile1 == nt;
+      const float lt0 = l0 + xor32(l0), lt1 = l1 + xor32(l1);
+      const bool has_tail = (S.n_keys & (BN - 1)) != 0;
+      const bool whole = tile0 == 0 && tile1 == nt && !has_tail;
       // piece slot of this unit: its k-th workgroup writes slot k
       const int k = w - wg_of_iter((long long)S.it_begin + (long long)u * nt, G, N);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int row = qrow0 + 32 * qb + l32;
         if (row >= S.rows) continue;
+        const f32x16& oa = qb == 0 ? o00 : o01;
+        const f32x16& ob = qb == 0 ? o10 : o11;
+        const float lt = qb == 0 ? lt0 : lt1;
+        const float mx = qb == 0 ? mx0 : mx1;
         if (whole) {
-          const float inv = 1.0f / lt[qb];
+          const float inv = 1.0f / lt;
           float* op = S.out + row * row_stride + h * D;
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              *reinterpret_cast<float4*>(op + 32 * db + 8 * q4 + 4 * g) =
-                  make_float4(o[db][qb][4 * q4] * inv, o[db][qb][4 * q4 + 1] * inv, o[db][qb][4 * q4 + 2] * inv,
-                              o[db][qb][4 * q4 + 3] * inv);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            *reinterpret_cast<float4*>(op + 8 * q4 + 4 * g) =
+                make_float4(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv, oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv);
+            *reinterpret_cast<float4*>(op + 32 + 8 * q4 + 4 * g) =
+                make_float4(ob[4 * q4] * inv, ob[4 * q4 + 1] * inv, ob[4 * q4 + 2] * inv, ob[4 * q4 + 3] * inv);
+          }
         } else {
           const size_t slot = (size_t)u * S.ppu + k;
           const int rin = row - qt * kSkRows;
           float* po = S.part_o + (slot * kSkRows + rin) * D;
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              *reinterpret_cast<float4*>(po + 32 * db + 8 * q4 + 4 * g) =
-                  make_float4(o[db][qb][4 * q4], o[db][qb][4 * q4 + 1], o[db][qb][4 * q4 + 2], o[db][qb][4 * q4 + 3]);
-          if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mx[qb], lt[qb]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            *reinterpret_cast<float4*>(po + 8 * q4 + 4 * g) =
+                make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
+            *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * g) =
+                make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
+          }
+          if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mx, lt);
         }
       }
     }
@@ -420,34 +536,133 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   }
 }
 
-// Merges the pieces of every unit that spans several workgroups.  One workgroup
-// per unit; thread t owns 8 float4 of the unit's 128 x 64 output (rows
-// t/16 + 16*i, columns 4*(t%16)).  Pieces are folded in one pass with a running
-// max, and each piece's loads for all 8 elements are issued together, so a unit
-// costs one global round trip per piece.
+// The tail of every unit whose key count is not a multiple of 64: the last keys % 64
+// keys, exact softmax over them (one tile, so the reference is the true max), written as
+// a partial to the unit's last scratch slot.  One workgroup per unit of the launch; wave
+// w holds query rows 32*w .. 32*w+31 of the unit.
+constexpr int kTailWaves = 4;
+__global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaunch a, int total_units) {
+  __shared__ __attribute__((aligned(16))) char st[STAGE];
+  const int ug = blockIdx.x;
+  if (ug >= total_units) return;
+  int si, u;
+  decode_unit(a, ug, si, u);
+  const SkSession& S = a.s[si];
+  const int nk = S.n_keys & (BN - 1);
+  if (nk == 0) return;  // no tail: uniform over the workgroup
+  const int key0 = S.n_keys - nk;
+  const int H = a.n_heads;
+  const float c = a.scale_log2;
+  const int qt = u % S.qtiles, h = u / S.qtiles;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int row_stride = H * D;
+  const int row_bytes = 2 * row_stride;
+  int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
+  seg_tables(S, seg_row, seg_key);
+
+  // the 64-row tile of keys key0 .. key0+63 (past the last key: its row again), wave w
+  // moving rows 16w .. 16w+15 of K and of V
+  {
+    const int drow = lane >> 3;
+    const int kchunk = (lane & 7) ^ drow;
+    const int vchunk = (lane & 7) ^ (2 * (drow & 3));
+    const char* kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
+    const char* vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int trow = 16 * wave + 8 * m;
+      const int kappa = min(key0 + trow + drow, S.n_keys - 1);
+      const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa) * row_bytes);
+      __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)(st + trow * ROW), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(st + TILE + trow * ROW), 16, 0, 0);
+    }
+  }
+  bf16x8 qop[4];
+  const int qrow = qt * kSkRows + 32 * wave + l32;
+  {
+    const int r = min(qrow, S.rows - 1);
+    const __bf16* qp = reinterpret_cast<const __bf16*>(S.q) + r * row_stride + h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+  }
+  __syncthreads();
+
+  SK_OPERAND_ADDRESSES(0);
+  const f32x16 zero16 = {};
+  f32x16 s[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    bf16x8 kop[4];
+    SK_LOAD_K(kop, st, 32 * hh);
+    SK_QK(s[hh], kop, qop);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (key >= nk) s[hh][r] = -INFINITY;
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) mt = max3(mt, max3(s[0][r], s[0][r + 1], s[1][r]), s[1][r + 1]);
+  const float mref = fmaxf(mt, xor32(mt)) * c;  // key 0 of the tail is real, so this is finite
+  f32x16 oa = zero16, ob = zero16;
+  float l = 0.0f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    bf16x8 vop[4], p[2];
+    SK_LOAD_V(vop, st, 32 * hh);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hh][8 * b + r], c, -mref));
+        p[b][r] = (__bf16)e;
+        l += e;
+      }
+    SK_PV(oa, ob, vop, p);
+  }
+  const float lt = l + xor32(l);
+  if (qrow < S.rows) {
+    const size_t slot = (size_t)u * S.ppu + (S.ppu - 1);
+    const int rin = qrow - qt * kSkRows;
+    float* po = S.part_o + (slot * kSkRows + rin) * D;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      *reinterpret_cast<float4*>(po + 8 * q4 + 4 * g) = make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
+      *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * g) =
+          make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
+    }
+    if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mref, lt);
+  }
+}
+
+// Merges the partials of every unit that has more than one: its pieces from
+// attn_sk_kernel (slots 0 .. last - first workgroup of the unit) and its tail (last
+// slot).  One workgroup per unit; thread t owns 8 float4 of the unit's 128 x 64 output
+// (rows t/16 + 16*i, columns 4*(t%16)).  Partials are folded in one pass with a running
+// max, and each partial's loads for all 8 elements are issued together, so a unit costs
+// one global round trip per partial.
 constexpr int kCombThreads = 256;
 constexpr int kCombPer = kSkRows * (D / 4) / kCombThreads;  // 8
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units) {
   const int ug = blockIdx.x;
   if (ug >= total_units) return;
-  int si = 0, ubase = 0;
-  {
-    int acc = 0;
-    for (int i = 0; i < a.n_sessions; ++i) {
-      if (ug >= acc) { si = i; ubase = acc; }
-      acc += a.n_heads * a.s[i].qtiles;
-    }
-  }
-  si = __builtin_amdgcn_readfirstlane(si);
-  ubase = __builtin_amdgcn_readfirstlane(ubase);
+  int si, u;
+  decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
-  const int u = ug - ubase;
   const int G = a.n_wg, N = a.n_iters;
-  const long long first = (long long)S.it_begin + (long long)u * S.ntiles;
-  const int wl = wg_of_iter(first, G, N);
-  const int wh = wg_of_iter(first + S.ntiles - 1, G, N);
-  if (wl == wh) return;  // written whole by one workgroup
-  const int pieces = wh - wl + 1;
+  const bool has_tail = (S.n_keys & (kSkKeys - 1)) != 0;
+  int pieces = 0;
+  if (S.ntiles > 0) {
+    const long long first = (long long)S.it_begin + (long long)u * S.ntiles;
+    pieces = wg_of_iter(first + S.ntiles - 1, G, N) - wg_of_iter(first, G, N) + 1;
+  }
+  if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
+  const int total = pieces + (has_tail ? 1 : 0);
   const int qt = u % S.qtiles, h = u / S.qtiles;
   const int H = a.n_heads;
   const int r0 = threadIdx.x / (D / 4);
@@ -461,8 +676,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
     l[i] = 0.0f;
     acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int k = 0; k < pieces; ++k) {
-    const size_t slot = (size_t)u * S.ppu + k;
+  for (int k = 0; k < total; ++k) {
+    const size_t slot = (size_t)u * S.ppu + (k < pieces ? k : S.ppu - 1);
     float2 ml[kCombPer];
     float4 x[kCombPer];
 #pragma unroll
@@ -474,7 +689,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
 #pragma unroll
     for (int i = 0; i < kCombPer; ++i) {
       const float mn = fmaxf(mx[i], ml[i].x);
-      const float fo = __builtin_amdgcn_exp2f(mx[i] - mn);  // mx = -inf on the first piece: 0
+      const float fo = __builtin_amdgcn_exp2f(mx[i] - mn);  // mx = -inf on the first partial: 0
       const float fn = __builtin_amdgcn_exp2f(ml[i].x - mn);
       l[i] = l[i] * fo + ml[i].y * fn;
       acc[i] = make_float4(acc[i].x * fo + x[i].x * fn, acc[i].y * fo + x[i].y * fn, acc[i].z * fo + x[i].z * fn,
@@ -495,7 +710,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
 }  // namespace
 
 int32_t sk_pieces_per_unit(int64_t capacity_rows) {
-  const int64_t nt = (capacity_rows + kSkKeys - 1) / kSkKeys;
+  // pieces of a unit: at most ceil(tiles / kSkMinRange) + 1 (every workgroup has at
+  // least kSkMinRange tiles); one more slot for the tail
+  const int64_t nt = capacity_rows / kSkKeys;
   return (int32_t)((nt + kSkMinRange - 1) / kSkMinRange + 2);
 }
 
@@ -506,6 +723,11 @@ size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows) {
 
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
   hipLaunchKernelGGL(attn_sk_kernel, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_tail_kernel, dim3(total_units), dim3(kTailWaves * 64), 0, stream, a, total_units);
   return hipGetLastError();
 }
 

@@ -343,6 +343,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     a.n_heads = H;
     a.scale_log2 = scale_log2;
     int64_t iters = 0, units_total = 0;
+    bool any_tail = false;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       Segs sg;
@@ -360,7 +361,8 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
         s.seg_len[j] = (int32_t)sg.len[j];
       }
       s.qtiles = (int32_t)((b->geo.R + sf::kSkRows - 1) / sf::kSkRows);
-      s.ntiles = (int32_t)((sg.keys + sf::kSkKeys - 1) / sf::kSkKeys);
+      s.ntiles = (int32_t)(sg.keys / sf::kSkKeys);
+      any_tail = any_tail || (sg.keys % sf::kSkKeys) != 0;
       s.ppu = sf::sk_pieces_per_unit(b->geo.C);
       const int64_t units = (int64_t)H * s.qtiles;
       s.part_o = reinterpret_cast<float*>(b->mem + b->geo.scratch_off);
@@ -376,12 +378,17 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     if (G >= 8) G -= G % 8;
     a.n_wg = (int32_t)G;
     a.n_iters = (int32_t)iters;
-    hipError_t e;
-    {
+    hipError_t e = hipSuccess;
+    if (iters > 0) {
       TraceScope ts(b0->trace, SF_K_ATTEND, st);
       e = sf::launch_attend_sk(a, st);
     }
     if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
+    if (any_tail) {
+      TraceScope ts(b0->trace, SF_K_TAIL, st);
+      e = sf::launch_tail_sk(a, (int)units_total, st);
+    }
+    if (e != hipSuccess) return hip_fail(b0, e, "attention tail launch");
     {
       TraceScope ts(b0->trace, SF_K_COMBINE, st);
       e = sf::launch_combine_sk(a, (int)units_total, st);

@@ -46,10 +46,11 @@ struct AttnLaunch {
 
 // ---- persistent stream-K attention (bf16, head_dim 64) ----------------------
 // The launch's work is the flattened sequence of (session, head, 128-row query
-// tile, 64-key tile) iterations; workgroup w takes iterations
+// tile, full 64-key tile) iterations; workgroup w takes iterations
 // [w*N/G, (w+1)*N/G).  A query tile that spans several workgroups leaves one
-// partial result per workgroup ("piece") in its session's scratch; the combine
-// kernel merges them.
+// partial result per workgroup ("piece") in its session's scratch; keys past the
+// last full tile (the tail) leave one more, from the tail kernel, in the unit's
+// last slot; the combine kernel merges them.
 constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
 constexpr int kSkMinRange = 8;      // fewest tiles a workgroup is given
@@ -64,7 +65,7 @@ struct SkSession {
   int32_t n_keys;       // readable rows
   int32_t n_seg;
   int32_t qtiles;       // ceil(rows / kSkRows)
-  int32_t ntiles;       // ceil(n_keys / kSkKeys)
+  int32_t ntiles;       // full key tiles: n_keys / kSkKeys
   int32_t ppu;          // piece slots per unit in the scratch
   int32_t it_begin;     // first iteration of this session in the launch
   int32_t pad;
@@ -85,6 +86,7 @@ struct SkLaunch {
 int32_t sk_pieces_per_unit(int64_t capacity_rows);
 size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows);
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream);
+hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream);
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream);
 
 // Query rows per workgroup of each attention kernel.

@@ -24,8 +24,11 @@ def test_kernel_times_count_every_launch():
     assert times["write"][1] == 2 * frames
     assert times["attend"][1] == 2 * frames
     assert times["combine"][1] == 2 * frames
+    # keys past the last full 64-key tile take one tail launch per read
+    tails = sum(1 for t in range(frames) if sf.sf_plan(sess.cfg, t)["n_keys"] % 64)
+    assert tails > 0 and times["tail"][1] == 2 * tails
     assert times["evict"][1] == frames - 4          # at t = 4, 5 frames 1, 2 leave RAW (Y = 2)
-    assert all(times[k][0] > 0.0 for k in ("write", "attend", "combine", "evict"))
+    assert all(times[k][0] > 0.0 for k in ("write", "attend", "combine", "evict", "tail"))
     again = sf.sf_kernel_times_read(sess.handle)   # a read starts a new period
     assert all(n == 0 for _, n in again.values())
     sf.sf_profile_enable(sess.handle, False)
