@@ -32,7 +32,7 @@
 // VGPRs), double buffered.
 //
 // Softmax with a fixed reference.  Each stream takes one reference per query,
-// the max of its first tile's scores, and keeps it: p = exp2(s*c - mref) may
+// the max of the scores of its first 32 keys, and keeps it: p = exp2(s*c - mref) may
 // exceed 1 but no rescaling of O is ever needed inside the loop, which is
 // therefore branch-free.  A lane's largest quarter sum is tracked; if in some
 // stream of the workgroup a p could have exceeded 2^40 (or overflowed), the
@@ -364,17 +364,13 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     };
 
     // Softmax with a reference fixed per query for the whole piece.  Attempt 0 takes the
-    // max of the stream's first tile; if some p could then have exceeded 2^40 (a lane's
+    // max of the stream's first 32 keys; if some p could then have exceeded 2^40 (a lane's
     // quarter sum above it, +inf included) anywhere in the workgroup, attempt 1 redoes the
     // piece with the exact max over each stream's keys, where every p is at most 1.
     for (int attempt = 0;; ++attempt) {
       float mt0 = -INFINITY, mt1 = -INFINITY;
-      if (attempt == 0) {
-        if (s_lo < s_hi) dma_tile(s_lo, st_a);
-        __syncthreads();
-        if (s_lo < s_hi && wave_on) tile_max(st_a, mt0, mt1);
-        __syncthreads();
-      } else {
+      if (attempt == 1) {
+        // exact maxima over the stream's tiles, then the first tile again
         if (s_lo < s_hi) dma_tile(s_lo, st_a);
         __syncthreads();
         for (int i = 0; i < steps; i += 2) {
@@ -387,11 +383,9 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
           if (tl + 1 < s_hi && wave_on) tile_max(st_b, mt0, mt1);
           __syncthreads();
         }
-        if (s_lo < s_hi) dma_tile(s_lo, st_a);  // the main loop starts from stage a
-        __syncthreads();
       }
-      mref0 = fmaxf(mt0, xor32(mt0)) * c;
-      mref1 = fmaxf(mt1, xor32(mt1)) * c;
+      if (s_lo < s_hi) dma_tile(s_lo, st_a);  // the stream's first tile, in stage a
+      __syncthreads();
       o00 = zero16;
       o10 = zero16;
       o01 = zero16;
@@ -400,7 +394,8 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       tsmax = 0.0f;
 
       // All waves take `steps` steps (uniform barriers); a wave whose stream has no tile
-      // at a step only takes part in the barriers.  The stream's first tile is in stage a.
+      // at a step only takes part in the barriers.  Attempt 0 takes the reference of each
+      // query from the first 32 keys of the stream (the scores the pipeline starts with).
       const bool run = s_lo < s_hi && wave_on;
       if (run) {
 #pragma unroll
@@ -414,7 +409,18 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
         }
         SK_LOAD_K(kop0, st_a, 0);
         SK_QK(sa, kop0, q0);
+        if (attempt == 0) {
+          f32x16 s1;
+          SK_QK(s1, kop0, q1);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            mt0 = max3(mt0, sa[r], sa[r + 1]);
+            mt1 = max3(mt1, s1[r], s1[r + 1]);
+          }
+        }
       }
+      mref0 = fmaxf(mt0, xor32(mt0)) * c;
+      mref1 = fmaxf(mt1, xor32(mt1)) * c;
       for (int i = 0; i < steps; i += 2) {
         const int tl = s_lo + i;
         if (tl + 1 < s_hi) dma_tile(tl + 1, st_b);
