@@ -23,6 +23,9 @@
 //   attn_tail_kernel: one workgroup per unit with a tail writes the tail's
 //     partial to the unit's last scratch slot;
 //   combine_sk_kernel: merges the partials of every unit that has more than one.
+// sf_step launches fold the record write in: the attention kernels read the new
+// record's keys from the caller's K/V (segment slot kRecSlot, after the buffer's
+// keys) and combine_sk_kernel copies the record into the buffer.
 //
 // Inside a workgroup of attn_sk_kernel.  Eight waves = four key streams x two
 // waves; the piece's tiles are cut into four contiguous quarters, one per
@@ -110,22 +113,33 @@ __device__ __forceinline__ void decode_unit(const SkLaunch& a, int ug, int& si, 
   u = __builtin_amdgcn_readfirstlane(ug - base);
 }
 
-// Buffer row of flattened key kappa (segments in ascending key order).
-__device__ __forceinline__ int key_row(const int* seg_row, const int* seg_key, int kappa) {
+// Row of flattened key kappa (segments in ascending key order) and its segment.  The
+// row counts in the buffer, or in the source of the record written by this launch for
+// that record's segment.
+__device__ __forceinline__ int key_row(const int* seg_row, const int* seg_key, int kappa, int& seg) {
   int row = seg_row[0] + kappa;
+  seg = 0;
 #pragma unroll
-  for (int i = 1; i < SF_MAX_SEGMENTS; ++i) row = kappa >= seg_key[i] ? seg_row[i] + (kappa - seg_key[i]) : row;
+  for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {
+    const bool in = kappa >= seg_key[i];
+    row = in ? seg_row[i] + (kappa - seg_key[i]) : row;
+    seg = in ? i : seg;
+  }
   return row;
 }
 
+// Segment i covers keys [seg_key[i], seg_key[i] + seg_len[i]) in slot order; an empty
+// slot starts where the next one does, so a lookup of the last slot whose start is at
+// or below a key never lands on it.  REC: the last slot holds the record's rows, which
+// are read from the caller's record (row 0 = its first row).
+template <bool REC>
 __device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int* seg_key) {
   int cum = 0;
 #pragma unroll
   for (int i = 0; i < SF_MAX_SEGMENTS; ++i) {
-    const bool used = i < S.n_seg;
-    seg_row[i] = used ? S.seg_begin[i] : 0;
-    seg_key[i] = used ? cum : 0x7fffffff;
-    cum += used ? S.seg_len[i] : 0;
+    seg_row[i] = (REC && i == kRecSlot) ? 0 : S.seg_begin[i];
+    seg_key[i] = cum;
+    cum += S.seg_len[i];
   }
 }
 
@@ -171,6 +185,7 @@ __device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int
     }                                                                                     \
   }
 
+template <bool REC>
 __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     const bool wave_on = qrow0 < S.rows;
 
     int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
-    seg_tables(S, seg_row, seg_key);
+    seg_tables<REC>(S, seg_row, seg_key);
 
     // Q^T operands: query block qb holds rows qrow0 + 32*qb + l32 (rows past R read row R-1).
     bf16x8 q0[4], q1[4];
@@ -242,36 +257,44 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
 
     const char* __restrict__ kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
     const char* __restrict__ vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
+    const char* __restrict__ krec = reinterpret_cast<const char*>(S.rec_k) + 2 * h * D;
+    const char* __restrict__ vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
 
     // Starts the transfer of this stream's tile TL into stage array ST (this wave's
     // half: rows [32*hw, 32*hw+32) of K and of V).  A tile inside one segment is a run
     // of rows (scalar base + fixed lane offsets); otherwise rows are looked up per lane.
     auto dma_tile = [&](const int tl, char* st) {
       const int kap0 = tl * BN;
-      int srow = seg_row[0], skey = seg_key[0], send = seg_key[1];
+      int srow = seg_row[0], skey = seg_key[0], send = seg_key[1], sidx = 0;
 #pragma unroll
       for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {
         const bool in = kap0 >= seg_key[i];
         srow = in ? seg_row[i] : srow;
         skey = in ? seg_key[i] : skey;
         send = in ? (i + 1 < SF_MAX_SEGMENTS ? seg_key[i + 1 < SF_MAX_SEGMENTS ? i + 1 : i] : 0x7fffffff) : send;
+        sidx = in ? i : sidx;
       }
       char* kdst = st + soff + (trow0 - drow) * ROW;
       char* vdst = kdst + TILE;
       if (kap0 + BN <= send) {
+        const char* kb = (REC && sidx == kRecSlot) ? krec : kg;
+        const char* vb = (REC && sidx == kRecSlot) ? vrec : vg;
         const unsigned base = (unsigned)((srow + kap0 - skey + trow0) * row_bytes);
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
           const unsigned rb = base + (unsigned)(m * DMA_ROWS * row_bytes);
-          __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
         }
       } else {
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
-          const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * DMA_ROWS) * row_bytes);
-          __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          int sg;
+          const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * DMA_ROWS, sg) * row_bytes);
+          const char* kb = (REC && sg == kRecSlot) ? krec : kg;
+          const char* vb = (REC && sg == kRecSlot) ? vrec : vg;
+          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
         }
       }
     };
@@ -568,7 +591,7 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
   const int row_stride = H * D;
   const int row_bytes = 2 * row_stride;
   int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
-  seg_tables(S, seg_row, seg_key);
+  seg_tables<false>(S, seg_row, seg_key);
 
   // the 64-row tile of keys key0 .. key0+63 (past the last key: its row again), wave w
   // moving rows 16w .. 16w+15 of K and of V
@@ -578,13 +601,18 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
     const int vchunk = (lane & 7) ^ (2 * (drow & 3));
     const char* kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
     const char* vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
+    const char* krec = reinterpret_cast<const char*>(S.rec_k) + 2 * h * D;
+    const char* vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int trow = 16 * wave + 8 * m;
       const int kappa = min(key0 + trow + drow, S.n_keys - 1);
-      const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa) * row_bytes);
-      __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)(st + trow * ROW), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(st + TILE + trow * ROW), 16, 0, 0);
+      int sg;
+      const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa, sg) * row_bytes);
+      const char* kb = (S.rec_seg >= 0 && sg == kRecSlot) ? krec : kg;
+      const char* vb = (S.rec_seg >= 0 && sg == kRecSlot) ? vrec : vg;
+      __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(st + trow * ROW), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(st + TILE + trow * ROW), 16, 0, 0);
     }
   }
   bf16x8 qop[4];
@@ -653,10 +681,40 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
 // max, and each partial's loads for all 8 elements are issued together, so a unit costs
 // one global round trip per partial.
 constexpr int kCombThreads = 256;
-constexpr int kCombPer = kSkRows * (D / 4) / kCombThreads;  // 8
+constexpr int kCombRows = 32;                                   // query rows per workgroup
+constexpr int kCombSplit = kSkRows / kCombRows;                 // workgroups per unit
+constexpr int kCombPer = kCombRows * (D / 4) / kCombThreads;    // rows per thread: 2
+constexpr int kCombBatch = 4;                                   // partials loaded at once
+static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kCombRows * (D / 4), "combine tiling");
+
+// Merges the partials of each unit that has more than one, in slot order (pieces, then
+// the tail), and writes the normalised output.  kCombSplit workgroups per unit, each
+// owning kCombRows rows; a thread owns 4 columns of kCombPer rows.  Partials are read
+// kCombBatch at a time, all loads in flight before the first is used.
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units) {
-  const int ug = blockIdx.x;
+  const int ug = blockIdx.x / kCombSplit;
+  const int part = blockIdx.x % kCombSplit;
   if (ug >= total_units) return;
+  // A record written by this launch (one session): the attention read its keys from the
+  // source, so the copy into the buffer can wait until now; its loads overlap the loads
+  // of the partials below.
+  if (a.n_sessions == 1 && a.s[0].rec_seg >= 0) {
+    const SkSession& S0 = a.s[0];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const size_t n16 = (size_t)S0.rows * a.n_heads * D * 2 / 16;
+    const size_t dst0 = (size_t)S0.rec_row0 * a.n_heads * D * 2 / 16;
+    const u32x4* __restrict__ sk = reinterpret_cast<const u32x4*>(S0.rec_k);
+    const u32x4* __restrict__ sv = reinterpret_cast<const u32x4*>(S0.rec_v);
+    u32x4* __restrict__ dk = reinterpret_cast<u32x4*>(const_cast<void*>(S0.k)) + dst0;
+    u32x4* __restrict__ dv = reinterpret_cast<u32x4*>(const_cast<void*>(S0.v)) + dst0;
+    const size_t nthr = (size_t)gridDim.x * kCombThreads;
+    for (size_t i = (size_t)blockIdx.x * kCombThreads + threadIdx.x; i < n16; i += nthr) {
+      const u32x4 x = __builtin_nontemporal_load(sk + i);
+      const u32x4 y = __builtin_nontemporal_load(sv + i);
+      __builtin_nontemporal_store(x, dk + i);
+      __builtin_nontemporal_store(y, dv + i);
+    }
+  }
   int si, u;
   decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
@@ -671,9 +729,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   const int total = pieces + (has_tail ? 1 : 0);
   const int qt = u % S.qtiles, h = u / S.qtiles;
   const int H = a.n_heads;
-  const int r0 = threadIdx.x / (D / 4);
+  constexpr int RSTRIDE = kCombThreads / (D / 4);  // 16 rows between a thread's rows
+  const int r0 = part * kCombRows + threadIdx.x / (D / 4);
   const int d4 = (threadIdx.x % (D / 4)) * 4;
-  constexpr int RSTRIDE = kCombThreads / (D / 4);  // 16 rows between a thread's elements
   float mx[kCombPer], l[kCombPer];
   float4 acc[kCombPer];
 #pragma unroll
@@ -682,25 +740,34 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
     l[i] = 0.0f;
     acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int k = 0; k < total; ++k) {
-    const size_t slot = (size_t)u * S.ppu + (k < pieces ? k : S.ppu - 1);
-    float2 ml[kCombPer];
-    float4 x[kCombPer];
+  for (int k0 = 0; k0 < total; k0 += kCombBatch) {
+    float2 ml[kCombBatch][kCombPer];
+    float4 x[kCombBatch][kCombPer];
 #pragma unroll
-    for (int i = 0; i < kCombPer; ++i) {
-      const int rin = r0 + RSTRIDE * i;
-      ml[i] = *reinterpret_cast<const float2*>(S.part_ml + (slot * kSkRows + rin) * 2);
-      x[i] = *reinterpret_cast<const float4*>(S.part_o + (slot * kSkRows + rin) * D + d4);
+    for (int j = 0; j < kCombBatch; ++j) {
+      const int k = k0 + j;
+      if (k >= total) break;
+      const size_t slot = (size_t)u * S.ppu + (k < pieces ? k : S.ppu - 1);
+#pragma unroll
+      for (int i = 0; i < kCombPer; ++i) {
+        const int rin = r0 + RSTRIDE * i;
+        ml[j][i] = *reinterpret_cast<const float2*>(S.part_ml + (slot * kSkRows + rin) * 2);
+        x[j][i] = *reinterpret_cast<const float4*>(S.part_o + (slot * kSkRows + rin) * D + d4);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < kCombPer; ++i) {
-      const float mn = fmaxf(mx[i], ml[i].x);
-      const float fo = __builtin_amdgcn_exp2f(mx[i] - mn);  // mx = -inf on the first partial: 0
-      const float fn = __builtin_amdgcn_exp2f(ml[i].x - mn);
-      l[i] = l[i] * fo + ml[i].y * fn;
-      acc[i] = make_float4(acc[i].x * fo + x[i].x * fn, acc[i].y * fo + x[i].y * fn, acc[i].z * fo + x[i].z * fn,
-                           acc[i].w * fo + x[i].w * fn);
-      mx[i] = mn;
+    for (int j = 0; j < kCombBatch; ++j) {
+      if (k0 + j >= total) break;
+#pragma unroll
+      for (int i = 0; i < kCombPer; ++i) {
+        const float mn = fmaxf(mx[i], ml[j][i].x);
+        const float fo = __builtin_amdgcn_exp2f(mx[i] - mn);  // mx = -inf on the first partial: 0
+        const float fn = __builtin_amdgcn_exp2f(ml[j][i].x - mn);
+        l[i] = l[i] * fo + ml[j][i].y * fn;
+        acc[i] = make_float4(acc[i].x * fo + x[j][i].x * fn, acc[i].y * fo + x[j][i].y * fn,
+                             acc[i].z * fo + x[j][i].z * fn, acc[i].w * fo + x[j][i].w * fn);
+        mx[i] = mn;
+      }
     }
   }
 #pragma unroll
@@ -728,7 +795,10 @@ size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows) {
 }
 
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_sk_kernel, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+  if (a.n_sessions == 1 && a.s[0].rec_seg >= 0)
+    hipLaunchKernelGGL(attn_sk_kernel<true>, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_sk_kernel<false>, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -738,7 +808,8 @@ hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream
 }
 
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_sk_kernel, dim3(total_units), dim3(kCombThreads), 0, stream, a, total_units);
+  hipLaunchKernelGGL(combine_sk_kernel, dim3(total_units * kCombSplit), dim3(kCombThreads), 0, stream, a,
+                     total_units);
   return hipGetLastError();
 }
 

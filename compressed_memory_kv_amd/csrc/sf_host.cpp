@@ -289,23 +289,37 @@ sf_status check_write(sf_buffer* b, int32_t block, int64_t t, const void* k, con
   return SF_OK;
 }
 
-sf_status apply_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st) {
-  const sf_config& c = b->cfg;
-  const int64_t row_bytes = b->geo.row_elems * elem_bytes(c.dtype);
-  const int64_t row0 = t == 0 ? 0 : b->geo.R * (1 + t % (c.y + 1));
-  if (take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
-  if (!b->dry) {
-    char* kb = b->mem + block * b->geo.block_stride + row0 * row_bytes;
-    char* vb = kb + b->geo.tensor_bytes;
-    TraceScope ts(b->trace, SF_K_WRITE, st);
-    hipError_t e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
-    if (e != hipSuccess) return hip_fail(b, e, "write launch");
-  }
+// First buffer row of frame t's record: Z0 or its RAW slot.
+int64_t record_row0(const sf_buffer* b, int64_t t) {
+  return t == 0 ? 0 : b->geo.R * (1 + t % (b->cfg.y + 1));
+}
+
+// The slot state after writing frame t's record into block `block`.
+void write_state(sf_buffer* b, int32_t block, int64_t t) {
   if (t != b->slots.t_cur) {
     b->slots.t_cur = t;
-    if (t >= 1) b->slots.raw_frame[t % (c.y + 1)] = t;
+    if (t >= 1) b->slots.raw_frame[t % (b->cfg.y + 1)] = t;
   }
   b->written_at[block] = t;
+}
+
+sf_status launch_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st) {
+  const int64_t row_bytes = b->geo.row_elems * elem_bytes(b->cfg.dtype);
+  char* kb = b->mem + block * b->geo.block_stride + record_row0(b, t) * row_bytes;
+  char* vb = kb + b->geo.tensor_bytes;
+  TraceScope ts(b->trace, SF_K_WRITE, st);
+  hipError_t e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
+  if (e != hipSuccess) return hip_fail(b, e, "write launch");
+  return SF_OK;
+}
+
+sf_status apply_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st) {
+  if (take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+  if (!b->dry) {
+    sf_status s = launch_write(b, block, t, k, v, st);
+    if (s != SF_OK) return s;
+  }
+  write_state(b, block, t);
   return SF_OK;
 }
 
@@ -331,8 +345,50 @@ int device_cu_count() {
 }
 
 // bf16, head_dim 64: persistent stream-K kernel, then the combine of split units.
+// A record that the attention launch writes itself (sf_step, bf16 head_dim 64): source
+// tensors and the buffer row it goes to.
+struct RecWrite {
+  const void* k;
+  const void* v;
+  int64_t row0;
+};
+
+// The readable segments with the record's rows [row0, row0 + rows) cut out as a segment
+// of their own whose rows count in the record's source; *rec_seg is its index (-1 if the
+// record is not inside one readable segment or the cut needs too many segments).
+Segs cut_record(const Segs& sg, int64_t row0, int64_t rows, int* rec_seg) {
+  // The buffer's readable rows without the record's, in slots 0.., and the record in
+  // slot kRecSlot.  Keys are summed in any order, so the record's keys go last.
+  Segs o;
+  *rec_seg = -1;
+  o.keys = sg.keys;
+  bool found = false;
+  auto add = [&](int64_t b, int64_t l) {
+    if (l <= 0) return true;
+    if (o.n >= sf::kRecSlot) return false;
+    o.begin[o.n] = b;
+    o.len[o.n] = l;
+    ++o.n;
+    return true;
+  };
+  for (int j = 0; j < sg.n; ++j) {
+    const int64_t b0 = sg.begin[j], e0 = b0 + sg.len[j];
+    if (!found && row0 >= b0 && row0 + rows <= e0) {
+      found = true;
+      if (!add(b0, row0 - b0) || !add(row0 + rows, e0 - row0 - rows)) return sg;
+    } else if (!add(b0, sg.len[j])) {
+      return sg;
+    }
+  }
+  if (!found) return sg;
+  o.begin[sf::kRecSlot] = 0;
+  o.len[sf::kRecSlot] = rows;
+  *rec_seg = sf::kRecSlot;
+  return o;
+}
+
 sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
-                            void* const* out, float scale_log2, hipStream_t st) {
+                            void* const* out, float scale_log2, hipStream_t st, const RecWrite* rec = nullptr) {
   sf_buffer* b0 = bufs[0];
   const int H = b0->cfg.n_heads;
   for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
@@ -349,6 +405,17 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       Segs sg;
       readable(b->cfg, b->geo, b->slots, &sg);
       sf::SkSession& s = a.s[i];
+      s.rec_seg = -1;
+      if (rec && n == 1) {
+        int rs = -1;
+        Segs cut = cut_record(sg, rec->row0, b->geo.R, &rs);
+        if (rs < 0) return fail(b0, SF_E_STATE, "sf_step: record rows are not readable");
+        sg = cut;
+        s.rec_seg = rs;
+        s.rec_k = rec->k;
+        s.rec_v = rec->v;
+        s.rec_row0 = (int32_t)rec->row0;
+      }
       s.q = q[first + i];
       s.out = static_cast<float*>(out[first + i]);
       s.k = b->mem + block * b->geo.block_stride;
@@ -356,7 +423,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.rows = (int32_t)b->geo.R;
       s.n_keys = (int32_t)sg.keys;
       s.n_seg = sg.n;
-      for (int j = 0; j < sg.n; ++j) {
+      for (int j = 0; j < SF_MAX_SEGMENTS; ++j) {
         s.seg_begin[j] = (int32_t)sg.begin[j];
         s.seg_len[j] = (int32_t)sg.len[j];
       }
@@ -371,7 +438,8 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       iters += units * s.ntiles;
       units_total += units;
     }
-    if (iters >= ((int64_t)1 << 30)) return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
+    if (iters >= ((int64_t)1 << 30) || units_total >= ((int64_t)1 << 28))
+      return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
     int64_t G = device_cu_count();
     if (G > iters / sf::kSkMinRange) G = iters / sf::kSkMinRange;
     if (G < 1) G = 1;
@@ -640,13 +708,35 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
     s = apply_evict(buf, t, ep, st);
     if (s != SF_OK) return restore(s);
   }
-  s = apply_write(buf, block, t, k, v, st);
-  if (s != SF_OK) return restore(s);
-  if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
-  if (buf->dry) return SF_OK;
   sf_buffer* one[1] = {buf};
   const void* qs[1] = {q};
   void* outs[1] = {out};
+  // bf16, head_dim 64: the attention launch writes the record itself (and reads its keys
+  // from k and v) whenever the block has a full 64-key tile after the write and the rows
+  // around the record fit the remaining segment slots.
+  if (!buf->dry && buf->cfg.dtype == SF_BF16 && buf->cfg.head_dim == 64) {
+    write_state(buf, block, t);
+    Segs sg;
+    readable(buf->cfg, buf->geo, buf->slots, &sg);
+    int rs = -1;
+    cut_record(sg, record_row0(buf, t), buf->geo.R, &rs);
+    if (sg.keys >= sf::kSkKeys && rs >= 0) {
+      if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
+      const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)buf->cfg.head_dim);
+      const RecWrite rw = {k, v, record_row0(buf, t)};
+      s = enqueue_attend_sk(one, 1, block, qs, outs, sc * 1.4426950408889634f, st, &rw);
+      if (s != SF_OK) return restore(s);
+      return SF_OK;
+    }
+    if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
+    s = launch_write(buf, block, t, k, v, st);
+    if (s != SF_OK) return restore(s);
+  } else {
+    s = apply_write(buf, block, t, k, v, st);
+    if (s != SF_OK) return restore(s);
+  }
+  if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
+  if (buf->dry) return SF_OK;
   s = enqueue_attend(one, 1, block, qs, outs, scale, st);
   if (s != SF_OK) return restore(s);
   return SF_OK;

@@ -54,6 +54,7 @@ struct AttnLaunch {
 constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
 constexpr int kSkMinRange = 8;      // fewest tiles a workgroup is given
+constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
   float* out;           // [rows][H][64] fp32
@@ -61,14 +62,22 @@ struct SkSession {
   const void* v;        // this block's V [C][H][64]
   float* part_o;        // [units][ppu][kSkRows][64] unnormalised partial numerators
   float* part_ml;       // [units][ppu][kSkRows][2] (reference max in log2 units, row sum)
+  // A record written by this launch (sf_step): its K/V are read from rec_k / rec_v
+  // (segment slot kRecSlot, rows counted from the record's first row, keys last) while
+  // combine_sk_kernel copies them into the buffer at row rec_row0.  rec_seg = kRecSlot
+  // when present, -1 otherwise.  Unused segment slots have length 0.
+  const void* rec_k;    // [rows][H][64] bf16
+  const void* rec_v;
+  int32_t rec_seg;
+  int32_t rec_row0;
   int32_t rows;         // query rows (R)
   int32_t n_keys;       // readable rows
-  int32_t n_seg;
+  int32_t n_seg;        // buffer segments in use (slots 0..n_seg-1)
   int32_t qtiles;       // ceil(rows / kSkRows)
   int32_t ntiles;       // full key tiles: n_keys / kSkKeys
   int32_t ppu;          // piece slots per unit in the scratch
   int32_t it_begin;     // first iteration of this session in the launch
-  int32_t pad;
+  int32_t pad[3];
   int32_t seg_begin[SF_MAX_SEGMENTS];
   int32_t seg_len[SF_MAX_SEGMENTS];
 };

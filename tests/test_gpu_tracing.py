@@ -16,10 +16,13 @@ def test_kernel_times_count_every_launch():
     out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
     sf.sf_profile_enable(sess.handle, True)
     frames = 6
-    for t in range(frames):
+    for t in range(frames):   # the separate calls: evict, then per block write and attend
+        if t >= 1:
+            sess.evict(t)
         for b in range(2):
             q, k, v = sf_inputs.frame_tensors(wl, 0, b, t, device="cuda")
-            sess.step(b, t, q, k, v, out)
+            sess.write_record(b, t, k, v)
+            sess.attend(b, q, out)
     times = sf.sf_kernel_times_read(sess.handle)
     assert times["write"][1] == 2 * frames
     assert times["attend"][1] == 2 * frames
@@ -31,4 +34,13 @@ def test_kernel_times_count_every_launch():
     assert all(times[k][0] > 0.0 for k in ("write", "attend", "combine", "evict", "tail"))
     again = sf.sf_kernel_times_read(sess.handle)   # a read starts a new period
     assert all(n == 0 for _, n in again.values())
+
+    # sf_step, bf16 head_dim 64: the attention launch writes the record itself
+    for t in range(frames, frames + 2):
+        for b in range(2):
+            q, k, v = sf_inputs.frame_tensors(wl, 0, b, t, device="cuda")
+            sess.step(b, t, q, k, v, out)
+    times = sf.sf_kernel_times_read(sess.handle)
+    assert times["write"][1] == 0
+    assert times["attend"][1] == 4 and times["evict"][1] == 2
     sf.sf_profile_enable(sess.handle, False)
