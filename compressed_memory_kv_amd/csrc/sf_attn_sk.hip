@@ -420,16 +420,19 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       // at a step only takes part in the barriers.  Attempt 0 takes the reference of each
       // query from the first 32 keys of the stream (the scores the pipeline starts with).
       const bool run = s_lo < s_hi && wave_on;
+      // The last quarter's operands start at zero in every wave: the compiler may issue
+      // the closing O^T MFMAs below without the stream's guard, and a stream without
+      // tiles must then add exactly zero (not whatever the registers held).
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vop1[q][e] = (__bf16)0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p3[0][e] = (__bf16)0.0f;
+        p3[1][e] = (__bf16)0.0f;
+      }
       if (run) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vop1[q][e] = (__bf16)0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p3[0][e] = (__bf16)0.0f;
-          p3[1][e] = (__bf16)0.0f;
-        }
         SK_LOAD_K(kop0, st_a, 0);
         SK_QK(sa, kop0, q0);
         if (attempt == 0) {
