@@ -218,7 +218,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("profiles/attn_sk_kernel.served_rollout.txt",
                                                  "compressed_memory_kv_amd/csrc/sf_attn_sk.hip"),
-                     "kernel": "attn_sk_kernel (head_dim 64 attention, stream-K)",
+                     "kernel": "attn_sk_kernel<true> (head_dim-64 attention of sf_step, stream-K)",
                      "flop_per_launch": attn_flop, "avg_launch_us": round(attn_avg_ms * 1e3, 3),
                      "launches": kt["attend"][1]},
         "attn_tflops": round(attn_tflops, 2),
