@@ -218,6 +218,27 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   SK_OPERAND_ADDRESSES(soff);
   const f32x16 zero16 = {};
 
+  // Q^T operands of the piece that starts at iteration it: query block qb holds rows
+  // qrow0 + 32*qb + l32 (rows past R read row R-1).  The next piece's are loaded as soon
+  // as the current piece's last S^T is done, so their latency hides behind the merge.
+  bf16x8 q0[4], q1[4];
+  auto load_q = [&](const int it) {
+    const SkSession& S = a.s[session_of_iter(a, it)];
+    const int u = __builtin_amdgcn_readfirstlane((it - S.it_begin) / S.ntiles);
+    const int qt = u % S.qtiles, h = u / S.qtiles;
+    const int qrow0 = qt * kSkRows + hw * 64;
+    const int r0 = min(qrow0 + l32, S.rows - 1);
+    const int r1 = min(qrow0 + 32 + l32, S.rows - 1);
+    const __bf16* qp0 = reinterpret_cast<const __bf16*>(S.q) + r0 * H * D + h * D + 8 * g;
+    const __bf16* qp1 = reinterpret_cast<const __bf16*>(S.q) + r1 * H * D + h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      q0[kk] = *reinterpret_cast<const bf16x8*>(qp0 + 16 * kk);
+      q1[kk] = *reinterpret_cast<const bf16x8*>(qp1 + 16 * kk);
+    }
+  };
+  if (it_lo < it_hi) load_q(it_lo);
+
   for (int it = it_lo; it < it_hi;) {
     // ---- the piece: one unit's tiles [tile0, tile1) inside this workgroup's range
     const int si = session_of_iter(a, it);
@@ -240,20 +261,6 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
 
     int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
     seg_tables<REC>(S, seg_row, seg_key);
-
-    // Q^T operands: query block qb holds rows qrow0 + 32*qb + l32 (rows past R read row R-1).
-    bf16x8 q0[4], q1[4];
-    {
-      const int r0 = min(qrow0 + l32, S.rows - 1);
-      const int r1 = min(qrow0 + 32 + l32, S.rows - 1);
-      const __bf16* qp0 = reinterpret_cast<const __bf16*>(S.q) + r0 * row_stride + h * D + 8 * g;
-      const __bf16* qp1 = reinterpret_cast<const __bf16*>(S.q) + r1 * row_stride + h * D + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        q0[kk] = *reinterpret_cast<const bf16x8*>(qp0 + 16 * kk);
-        q1[kk] = *reinterpret_cast<const bf16x8*>(qp1 + 16 * kk);
-      }
-    }
 
     const char* __restrict__ kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
     const char* __restrict__ vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
@@ -473,6 +480,8 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       __syncthreads();
       if (!__builtin_amdgcn_readfirstlane(any_bad) || attempt == 1) break;
     }
+
+    if (it + (tile1 - tile0) < it_hi) load_q(it + (tile1 - tile0));  // the next piece's Q
 
     // ---- merge the four streams (stream 0 collects), then write
     auto merge_slot = [&](const int sl) -> float* {
