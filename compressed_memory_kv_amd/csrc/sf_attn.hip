@@ -57,10 +57,11 @@ constexpr int BM = kBf16RowsPerTile;  // 128 query rows per workgroup
 constexpr int BN = kBf16KeysPerTile;  // 64 keys per tile
 static_assert(BM == kWaves * 32, "one 32-row MFMA block per wave");
 
-// Work unit of this workgroup: XCD-aware remap of blockIdx.x.
-__device__ __forceinline__ int unit_of_block() {
-  const int per_xcd = gridDim.x >> 3;  // grid is a multiple of 8
-  return (int)(blockIdx.x & 7u) * per_xcd + (int)(blockIdx.x >> 3);
+// Work unit of this workgroup: XCD-aware remap of the workgroup id; the grid is
+// total_units rounded up to a multiple of 8.
+__device__ __forceinline__ int unit_of_block(int total_units) {
+  const int per_xcd = ((total_units + 7) & ~7) >> 3;
+  return (int)(wg_x() & 7u) * per_xcd + (int)(wg_x() >> 3);
 }
 
 // Everything a workgroup needs about its unit, wave-uniform (held in SGPRs).
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   static_assert(PER * kThreads == BN * CH, "tile loads divide evenly");
   __shared__ __attribute__((aligned(16))) char sm[2 * T::STAGE];
 
-  const int unit = unit_of_block();
+  const int unit = unit_of_block(a.total_units);
   if (unit >= a.total_units) return;
   const Unit U = decode_unit(a, unit, true);
   const int H = a.n_heads;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   const int t1 = __builtin_amdgcn_readfirstlane((int)((long long)(U.ks + 1) * ntiles / U.split));
   const int key_hi = min(t1 * BN, U.n_keys);
 
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5;   // lane half: k-group of MFMA operands
@@ -385,12 +386,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
 // Merge key splits: one wave per (row, head); lane covers D/64 output columns.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnLaunch a) {
-  const AttnSession& S = a.s[blockIdx.y];
+  const AttnSession& S = a.s[wg_y()];
   if (S.split <= 1) return;
   const int H = a.n_heads;
-  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int idx = wg_x() * 4 + (tid_x() >> 6);
   if (idx >= S.rows * H) return;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_x() & 63;
   const size_t slice = (size_t)S.rows * H;  // (row, head) pairs per split
   float mmax = -INFINITY;
   for (int k = 0; k < S.split; ++k) mmax = fmaxf(mmax, S.part_ml[(k * slice + idx) * 2]);
@@ -420,11 +421,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
   constexpr int KT = D <= 64 ? 16 : 8;  // keys per LDS tile
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
-  const int unit = (int)blockIdx.x;
+  const int unit = (int)wg_x();
   if (unit >= a.total_units) return;
   const Unit U = decode_unit(a, unit, false);
   const int H = a.n_heads;
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int qrow = U.qt * kF32RowsPerTile + tid;
   const bool row_ok = qrow < U.rows;
   const int row_stride = H * D;

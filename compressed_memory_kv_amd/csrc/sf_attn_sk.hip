@@ -192,13 +192,13 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   __shared__ int redo[kWaves];
   const int G = a.n_wg;
   const int N = a.n_iters;
-  const int w = (G & 7) == 0 ? (int)(blockIdx.x & 7u) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int w = (G & 7) == 0 ? (int)(wg_x() & 7u) * (G >> 3) + (int)(wg_x() >> 3) : (int)wg_x();
   const int it_lo = __builtin_amdgcn_readfirstlane((int)((long long)w * N / G));
   const int it_hi = __builtin_amdgcn_readfirstlane((int)((long long)(w + 1) * N / G));
   const int H = a.n_heads;
   const float c = a.scale_log2;
 
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int stream = wave >> 1;   // key stream
   const int hw = wave & 1;        // which 64 query rows of the unit
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
 constexpr int kTailWaves = 4;
 __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaunch a, int total_units) {
   __shared__ __attribute__((aligned(16))) char st[STAGE];
-  const int ug = blockIdx.x;
+  const int ug = wg_x();
   if (ug >= total_units) return;
   int si, u;
   decode_unit(a, ug, si, u);
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
   const int H = a.n_heads;
   const float c = a.scale_log2;
   const int qt = u % S.qtiles, h = u / S.qtiles;
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5;
@@ -704,8 +704,8 @@ static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kC
 // owning kCombRows rows; a thread owns 4 columns of kCombPer rows.  Partials are read
 // kCombBatch at a time, all loads in flight before the first is used.
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units) {
-  const int ug = blockIdx.x / kCombSplit;
-  const int part = blockIdx.x % kCombSplit;
+  const int ug = wg_x() / kCombSplit;
+  const int part = wg_x() % kCombSplit;
   if (ug >= total_units) return;
   // A record written by this launch (one session): the attention read its keys from the
   // source, so the copy into the buffer can wait until now; its loads overlap the loads
@@ -719,8 +719,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
     const u32x4* __restrict__ sv = reinterpret_cast<const u32x4*>(S0.rec_v);
     u32x4* __restrict__ dk = reinterpret_cast<u32x4*>(const_cast<void*>(S0.k)) + dst0;
     u32x4* __restrict__ dv = reinterpret_cast<u32x4*>(const_cast<void*>(S0.v)) + dst0;
-    const size_t nthr = (size_t)gridDim.x * kCombThreads;
-    for (size_t i = (size_t)blockIdx.x * kCombThreads + threadIdx.x; i < n16; i += nthr) {
+    const size_t nthr = (size_t)total_units * kCombSplit * kCombThreads;  // the whole grid
+    for (size_t i = (size_t)wg_x() * kCombThreads + tid_x(); i < n16; i += nthr) {
       const u32x4 x = __builtin_nontemporal_load(sk + i);
       const u32x4 y = __builtin_nontemporal_load(sv + i);
       __builtin_nontemporal_store(x, dk + i);
@@ -742,8 +742,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   const int qt = u % S.qtiles, h = u / S.qtiles;
   const int H = a.n_heads;
   constexpr int RSTRIDE = kCombThreads / (D / 4);  // 16 rows between a thread's rows
-  const int r0 = part * kCombRows + threadIdx.x / (D / 4);
-  const int d4 = (threadIdx.x % (D / 4)) * 4;
+  const int r0 = part * kCombRows + tid_x() / (D / 4);
+  const int d4 = (tid_x() % (D / 4)) * 4;
   float mx[kCombPer], l[kCombPer];
   float4 acc[kCombPer];
 #pragma unroll

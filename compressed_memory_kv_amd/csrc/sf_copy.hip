@@ -23,7 +23,7 @@ constexpr size_t kPerBlock = (size_t)kThreads * kVec;  // vectors per workgroup
 
 __device__ __forceinline__ void copy_chunk(u32x4* __restrict__ d, const u32x4* __restrict__ s, size_t first,
                                            size_t n16) {
-  const size_t i = first + threadIdx.x;
+  const size_t i = first + tid_x();
   if (first + kPerBlock <= n16) {
     // the source is not read again: stream it past the caches
     const u32x4 a0 = __builtin_nontemporal_load(s + i);
@@ -40,8 +40,8 @@ __device__ __forceinline__ void copy_chunk(u32x4* __restrict__ d, const u32x4* _
 }
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(u32x4* __restrict__ p, size_t n16) {
-  const size_t first = (size_t)blockIdx.x * kPerBlock;
-  const size_t i = first + threadIdx.x;
+  const size_t first = (size_t)wg_x() * kPerBlock;
+  const size_t i = first + tid_x();
   const u32x4 z = {0u, 0u, 0u, 0u};
   if (first + kPerBlock <= n16) {
     p[i] = z;
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void copy_pair_kernel(u32x4* __restrict__
                                                              const u32x4* __restrict__ sk,
                                                              const u32x4* __restrict__ sv, size_t n16,
                                                              unsigned per) {
-  const bool second = blockIdx.x >= per;
-  const unsigned b = second ? blockIdx.x - per : blockIdx.x;
+  const bool second = wg_x() >= per;
+  const unsigned b = second ? wg_x() - per : wg_x();
   copy_chunk(second ? dv : dk, second ? sv : sk, (size_t)b * kPerBlock, n16);
 }
 
@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kThreads) void copy_pair_kernel(u32x4* __restrict__
 __global__ __launch_bounds__(kThreads) void evict_kernel(char* __restrict__ mem, size_t block_stride,
                                                          size_t v_offset, size_t src_off, size_t dst_off,
                                                          size_t n16, unsigned per) {
-  const unsigned copy = blockIdx.x / per;
-  const unsigned b = blockIdx.x - copy * per;
+  const unsigned copy = wg_x() / per;
+  const unsigned b = wg_x() - copy * per;
   char* base = mem + (size_t)(copy >> 1) * block_stride + ((copy & 1u) ? v_offset : 0);
   copy_chunk(reinterpret_cast<u32x4*>(base + dst_off), reinterpret_cast<const u32x4*>(base + src_off),
              (size_t)b * kPerBlock, n16);

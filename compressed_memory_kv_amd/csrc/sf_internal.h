@@ -11,6 +11,14 @@
 
 namespace sf {
 
+// Work-item and workgroup ids read straight from the hardware.  HIP's threadIdx and
+// blockIdx go through device-library functions built with packed fp32 ops on; code built
+// with them off cannot inline those (the callee's target features are not a subset of
+// the caller's), so each use would be a real call: a stack, saved registers and spills.
+__device__ __forceinline__ unsigned tid_x() { return __builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ unsigned wg_x() { return __builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ unsigned wg_y() { return __builtin_amdgcn_workgroup_id_y(); }
+
 // Most sessions one attention launch covers; sf_attend splits larger batches.
 constexpr int kMaxLaunchSessions = 16;
 // Most key splits per (session, head, query tile); bounds the scratch region.
