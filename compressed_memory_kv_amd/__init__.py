@@ -36,14 +36,15 @@ EXPORTED = (
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
 )
-SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_KINDS = 0, 1, 2, 3, 4, 5, 6
-KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail")
+SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_KINDS = range(8)
+KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink")
 
 
 class sf_config(ctypes.Structure):
     _fields_ = [("hw", ctypes.c_int32), ("x", ctypes.c_int32), ("y", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("max_frames", ctypes.c_int64)]
+                ("dtype", ctypes.c_int32), ("max_frames", ctypes.c_int64), ("sink_gap", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 class sf_view(ctypes.Structure):
@@ -51,7 +52,7 @@ class sf_view(ctypes.Structure):
                 ("n_seg", ctypes.c_int32), ("raw_slot", ctypes.c_int32), ("blocks_written", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("seg_begin", ctypes.c_int64 * SF_MAX_SEGMENTS),
                 ("seg_len", ctypes.c_int64 * SF_MAX_SEGMENTS), ("raw_frame", ctypes.POINTER(ctypes.c_int64)),
-                ("sum_frame", ctypes.POINTER(ctypes.c_int64))]
+                ("sum_frame", ctypes.POINTER(ctypes.c_int64)), ("z0_frame", ctypes.c_int64)]
 
 
 class sf_kernel_times(ctypes.Structure):
@@ -122,10 +123,11 @@ def _stream(s) -> int | None:
     return s.cuda_stream
 
 
-def make_config(hw, x, y, w, n_heads, head_dim, n_blocks=1, dtype="bf16", max_frames=0, **_ignored) -> sf_config:
+def make_config(hw, x, y, w, n_heads, head_dim, n_blocks=1, dtype="bf16", max_frames=0, sink_gap=0,
+                rope_theta=10000.0, **_ignored) -> sf_config:
     """sf_config from keyword fields (extra keys, e.g. of a workload dict, are ignored)."""
     return sf_config(hw, x, y, w, n_heads, head_dim, n_blocks, DTYPES[dtype] if isinstance(dtype, str) else dtype,
-                     max_frames)
+                     max_frames, sink_gap, rope_theta)
 
 
 # --------------------------------------------------------------- the C calls
@@ -183,7 +185,7 @@ def _view_dict(v: sf_view, raw, summ) -> dict:
         "t_cur": v.t_cur, "n_keys": v.n_keys, "evicted_for": v.evicted_for, "raw_slot": v.raw_slot,
         "blocks_written": v.blocks_written,
         "segments": [(v.seg_begin[i], v.seg_len[i]) for i in range(v.n_seg)],
-        "raw_frame": list(raw), "sum_frame": list(summ),
+        "raw_frame": list(raw), "sum_frame": list(summ), "z0_frame": v.z0_frame,
     }
 
 

@@ -47,6 +47,10 @@ sf_status check_config(const sf_config* c, std::string* why) {
     return SF_E_ARG;
   }
   if (c->dtype != SF_F32 && c->dtype != SF_BF16) { *why = "dtype must be SF_F32 or SF_BF16"; return SF_E_ARG; }
+  if (c->sink_gap < 0 || c->sink_gap == 1 || (c->sink_gap > 0 && !(c->rope_theta > 1.0f))) {
+    *why = "sink_gap must be 0 (off) or >= 2, with rope_theta > 1";
+    return SF_E_ARG;
+  }
   if (c->head_dim != 64 && c->head_dim != 128) { *why = "head_dim must be 64 or 128"; return SF_E_UNSUPPORTED; }
   if (c->y + 1 > 4096 || c->w - c->y > (1 << 20) || c->n_blocks > 4096 || c->n_heads > 4096) {
     *why = "config too large (y+1 <= 4096, w-y <= 2^20, n_blocks <= 4096, n_heads <= 4096)";
@@ -82,9 +86,41 @@ Geo geometry(const sf_config* c) {
 struct Slots {
   int64_t t_cur = -1;
   int64_t evicted_for = -1;
+  int64_t z0_frame = 0;            // frame id Z0's keys are rotated to ([sink])
   std::vector<int64_t> raw_frame;  // frame in each RAW slot, -1 empty
   std::vector<int64_t> sum_frame;  // frame summarised in each SUM slot, -1 empty
 };
+
+// [sink] The shift T by which Z0's keys turn after an eviction step: when the oldest
+// generated frame in memory is sink_gap or more frames past Z0's frame id, back to a
+// gap of 1.  0: nothing to do.
+int64_t sink_shift(const sf_config& c, const Slots& s) {
+  if (c.sink_gap <= 0) return 0;
+  int64_t oldest = -1;
+  for (int64_t f : s.raw_frame)
+    if (f >= 1 && (oldest < 0 || f < oldest)) oldest = f;
+  for (int64_t f : s.sum_frame)
+    if (f >= 1 && (oldest < 0 || f < oldest)) oldest = f;
+  if (oldest < 0 || oldest - s.z0_frame < c.sink_gap) return 0;
+  return oldest - 1 - s.z0_frame;
+}
+
+// [sink] Temporal planes of a head in the rotary table (Wan2.1 split: the temporal
+// band takes hd - 4*floor(hd/6) dims, first in the head) and their cosines and sines
+// for a shift of T frames.
+sf::SinkTable sink_table(const sf_config& c, int64_t T) {
+  sf::SinkTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  const int dim_t = c.head_dim - 4 * (c.head_dim / 6);
+  tab.n_planes = dim_t / 2;
+  for (int i = 0; i < tab.n_planes; ++i) {
+    const double omega = std::pow((double)c.rope_theta, -2.0 * i / dim_t);
+    const double a = omega * (double)T;
+    tab.c[i] = (float)std::cos(a);
+    tab.s[i] = (float)std::sin(a);
+  }
+  return tab;
+}
 
 struct Segs {
   int n = 0;
@@ -266,6 +302,17 @@ sf_status apply_evict(sf_buffer* b, int64_t t, const EvictPlan& p, hipStream_t s
   }
   if (p.copy) b->slots.sum_frame[p.u] = p.f;
   b->slots.evicted_for = t;
+  const int64_t T = sink_shift(c, b->slots);
+  if (T > 0) {
+    if (take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+    if (!b->dry) {
+      TraceScope ts(b->trace, SF_K_SINK, st);
+      hipError_t e = sf::launch_sink_rotate(b->mem, c.n_blocks, (size_t)b->geo.block_stride, (int)b->geo.R,
+                                            c.n_heads, c.head_dim, c.dtype == SF_BF16, sink_table(c, T), st);
+      if (e != hipSuccess) return hip_fail(b, e, "sink rotation launch");
+    }
+    b->slots.z0_frame += T;
+  }
   return SF_OK;
 }
 
@@ -566,6 +613,7 @@ void fill_view(const sf_config& c, const Geo& g, const Slots& s, int32_t blocks_
     for (int i = 0; i <= c.y; ++i) v->raw_frame[i] = s.raw_frame[i];
   if (v->sum_frame)
     for (int i = 0; i < c.w - c.y; ++i) v->sum_frame[i] = s.sum_frame[i];
+  v->z0_frame = s.z0_frame;
 }
 
 }  // namespace
@@ -768,6 +816,7 @@ sf_status sf_plan(const sf_config* cfg, int64_t t, sf_view* view) {
       const int64_t leaving = s.raw_frame[sl];
       if (leaving >= 1) s.sum_frame[leaving % (cfg->w - cfg->y)] = leaving;
     }
+    if (f >= 1) s.z0_frame += sink_shift(*cfg, s);
     if (f >= 1) s.raw_frame[f % (cfg->y + 1)] = f;
     if (f >= 1) s.evicted_for = f;
     s.t_cur = f;

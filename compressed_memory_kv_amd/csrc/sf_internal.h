@@ -122,6 +122,18 @@ hipError_t launch_copy_rows(void* dst_k, void* dst_v, const void* src_k, const v
 // block b's K starts at mem + b*block_stride, its V at that + v_offset.
 hipError_t launch_evict(void* mem, int n_blocks, size_t block_stride, size_t v_offset,
                         size_t src_off, size_t dst_off, size_t bytes, hipStream_t stream);
+// Streaming sink: rotates the first n_planes (dim 2i, 2i+1) planes of every head of the
+// first `rows` K rows of every block (K of block b at mem + b*block_stride) by the
+// angle with cosine c[i] and sine s[i].
+constexpr int kSinkMaxPlanes = 32;
+struct SinkTable {
+  int32_t n_planes;
+  int32_t pad;
+  float c[kSinkMaxPlanes];
+  float s[kSinkMaxPlanes];
+};
+hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int rows, int heads, int head_dim,
+                              bool bf16, const SinkTable& tab, hipStream_t stream);
 hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream);

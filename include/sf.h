@@ -15,6 +15,12 @@
  *              rewrites the frame's entry in memory.
  *   [limits]   "Limits": sessions end at the last frame id of the position
  *              table (4096 ids on the page).
+ *   [sink]     "Running for a long time: the start image follows the window":
+ *              Z0's stored keys are moved forward in time by one more RoPE
+ *              rotation, in place, whenever the gap to the oldest frame in
+ *              memory reaches 5; values are untouched.  With "Telling a summary
+ *              from a pixel: level planes" (12 temporal planes per head) and
+ *              the "Positions" item (a rotary table adapted from Wan2.1).
  *
  * Terms.  A session is one player's memory: n_blocks independent buffers,
  * one per transformer block, stepped together frame by frame.  R = hw + x
@@ -84,6 +90,11 @@ typedef struct sf_config {
   int32_t n_blocks;   /* transformer blocks, one buffer each, >= 1 */
   int32_t dtype;      /* sf_dtype of q, k, v and of the stored K/V */
   int64_t max_frames; /* frame ids must stay below this ([limits]); 0 = no cap */
+  int32_t sink_gap;   /* [sink] 0 = off; else >= 2: when the oldest generated frame still in
+                         memory is sink_gap frames past Z0's frame id, Z0's keys are rotated
+                         forward to bring the gap back to 1 (the page uses 5) */
+  float rope_theta;   /* [sink] base of the temporal RoPE band the stored keys carry (> 1;
+                         the page's table follows Wan2.1: 10000); read only when sink_gap > 0 */
 } sf_config;
 
 #define SF_MAX_SEGMENTS 4
@@ -102,6 +113,7 @@ typedef struct sf_view {
   int64_t seg_len[SF_MAX_SEGMENTS];
   int64_t* raw_frame;   /* in: caller array of y+1 entries or NULL; out: frame id per RAW slot (-1 empty) */
   int64_t* sum_frame;   /* in: caller array of w-y entries or NULL; out: frame id per SUM slot (-1 empty) */
+  int64_t z0_frame;     /* [sink] frame id Z0's keys are rotated to (0 until the first rotation) */
 } sf_view;
 
 typedef struct sf_buffer sf_buffer;
@@ -139,7 +151,13 @@ sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* 
  * (record rows [hw, R)) of the frame leaving RAW slot t mod (y+1) into its SUM slot
  * f mod (w-y), in every block, in one launch.  The raw rows are not copied.  t must be
  * t_cur + 1 with every block holding t_cur.  A no-op when no generated frame leaves (t <= y+1);
- * repeating it for the same t is a no-op. */
+ * repeating it for the same t is a no-op.
+ * [sink] With sink_gap > 0, once this step's eviction is done: if the oldest generated frame
+ * in memory is now sink_gap or more frames past Z0's frame id z, every block's Z0 keys (all R
+ * rows, all heads; values untouched) are rotated in place by rotation(T), T = oldest - 1 - z,
+ * on the temporal RoPE planes, and z advances by T.  Plane i (dims 2i, 2i+1 of a head, i below
+ * hd/2 - 2*floor(hd/6)) turns by T * rope_theta^(-2i / (hd - 4*floor(hd/6))); the rotation is
+ * done in fp32 and rounded to the storage type. */
 sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
 
 /* [attends], [buffer] The dense read.  For each of n sessions (n <= SF_MAX_BATCH; equal
@@ -177,8 +195,10 @@ sf_status sf_debug_fail_next_launch(sf_buffer* buf);
  * for it is bracketed by two HIP events on the caller's stream.  sf_kernel_times waits for
  * those events, returns the summed milliseconds and launch counts per kind since the last
  * read, and starts a new period.  Kinds (ATTEND: the main attention kernel; TAIL: keys past the
- * last full 64-key tile of a bf16 head_dim-64 read; COMBINE: merging of split results): */
-enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_TAIL = 5, SF_K_KINDS = 6 };
+ * last full 64-key tile of a bf16 head_dim-64 read; COMBINE: merging of split results; SINK:
+ * the rotation of Z0's keys): */
+enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_TAIL = 5,
+       SF_K_SINK = 6, SF_K_KINDS = 7 };
 typedef struct sf_kernel_times {
   double ms[SF_K_KINDS];
   int64_t launches[SF_K_KINDS];

@@ -25,6 +25,17 @@ this file name its parts:
              the parameter table and the dense, unmasked read.
   [sampling] section "The rest of the model", the "Sampling" item: a clean
              pass rewrites the frame's entry in memory.
+  [sink]     section "Running for a long time: the start image follows the
+             window": rotary keys compose, rotation(id + T) = rotation(id) *
+             rotation(T); when the gap between the start image and the oldest
+             frame in memory reaches 5, the start image's keys are rotated
+             forward to bring it back to 1, values untouched.
+  [level]    section "Telling a summary from a pixel: level planes": 12
+             temporal planes per head; the two slowest turn by less than half
+             a radian over 1024 frames.
+  [positions] section "The rest of the model", the "Positions" item: one
+             rotary table with temporal, height and width bands, indexed in
+             time by frame id, adapted from Wan2.1.
 
 Readings where the page leaves a step open (each is listed in the design doc):
   * Frame 0 is the start image and lives in Z0; generated frames are t >= 1.
@@ -32,12 +43,25 @@ Readings where the page leaves a step open (each is listed in the design doc):
   * In one step, the eviction runs before the new record is written.
   * Softmax scale defaults to 1/sqrt(head_dim).
   * Empty slots hold zeros and are never read.
+  * [sink] The temporal band is laid out as in Wan2.1's table (which
+    [positions] credits): the first hd/2 - 2*floor(hd/6) complex planes of a
+    head, plane i being dims (2i, 2i+1) as (real, imaginary), turning at
+    theta^(-2i / (hd - 4*floor(hd/6))) radians per frame, theta = 10000.
+    This gives the 12 temporal planes of [level] at head_dim 64, and exactly
+    its two slowest stay under half a radian over 1024 frames.
+  * [sink] "The oldest frame in memory" is the oldest generated frame held in
+    a RAW or SUM slot; the check runs after each frame's eviction step (the
+    only time that frame can change), and the rotation turns every Z0 key row
+    (raw and summary rows of the start image) on all temporal planes by
+    rotation(T), T = oldest - 1 - (Z0's frame id).
 
 Pin status.  Every function below is pinned by tests/test_oracle_pins.py
 against facts the page fixes (the figure's worked example, the caption's key
 counts, brute-force equality with the attention-set rule, closed forms of
-softmax attention, torch's float64 SDPA over gathered rows).  No function
-here is "parity unpinned".
+softmax attention, torch's float64 SDPA over gathered rows, the 12 temporal
+planes and the half-radian bound of [level], the composition law of [sink],
+numpy's float32 conversion for the rounding).  No function here is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -117,6 +141,29 @@ def stored_to_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return bf16_bits_to_f64(a)
     return np.asarray(a, dtype=np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of fp64 values, rounded once to nearest (ties to even).
+
+    Finite values only.  The significand is scaled to 8 bits, rounded with
+    numpy's rint (ties to even) and the exact result converted to float32,
+    whose upper 16 bits are the bfloat16 pattern; below 2**-126 the quantum
+    is the subnormal step 2**-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # subnormal range: fixed quantum 2**-133
+    r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    bits = r.astype(np.float32).view(np.uint32)
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+def f64_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored form of fp64 values: bfloat16 bits (single rounding) or float32."""
+    if dtype == "bf16":
+        return f64_to_bf16_bits(x)
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
 
 
 def default_scale(head_dim: int) -> float:
@@ -207,6 +254,44 @@ def key_count(g: Geometry, t: int) -> int:
 
 
 # --------------------------------------------------------------------------
+# Rotary temporal band and the streaming sink ([sink], [level], [positions])
+# --------------------------------------------------------------------------
+def temporal_planes(head_dim: int) -> int:
+    """Temporal planes per head: the band Wan2.1's table gives time,
+    hd - 4*floor(hd/6) dims, counted in planes of two dims."""
+    return (head_dim - 4 * (head_dim // 6)) // 2
+
+
+def temporal_frequencies(head_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """Radians per frame of temporal plane i: theta^(-2i / band dims)."""
+    n = temporal_planes(head_dim)
+    return theta ** (-(2.0 * np.arange(n)) / (2 * n))
+
+
+def rotate_temporal(k: np.ndarray, head_dim: int, frames: float, theta: float = 10000.0) -> np.ndarray:
+    """Keys moved ``frames`` forward in time: every temporal plane (x, y) of every
+    head turned by its frequency times ``frames``, as the complex product
+    (x + iy) * exp(i a).  k: [..., head_dim] fp64; returns a new fp64 array."""
+    out = np.array(k, dtype=np.float64, copy=True)
+    n = temporal_planes(head_dim)
+    a = temporal_frequencies(head_dim, theta) * frames
+    x = out[..., 0:2 * n:2].copy()
+    y = out[..., 1:2 * n:2].copy()
+    c, s = np.cos(a), np.sin(a)
+    out[..., 0:2 * n:2] = x * c - y * s
+    out[..., 1:2 * n:2] = x * s + y * c
+    return out
+
+
+def sink_shift(oldest: int, z0_frame: int, gap: int) -> int:
+    """[sink] Frames Z0 moves forward after an eviction step: back to a gap of 1
+    once the gap to the oldest generated frame in memory reaches ``gap``."""
+    if gap <= 0 or oldest < 1 or oldest - z0_frame < gap:
+        return 0
+    return oldest - 1 - z0_frame
+
+
+# --------------------------------------------------------------------------
 # The buffer replay
 # --------------------------------------------------------------------------
 class MemoryReplay:
@@ -219,8 +304,11 @@ class MemoryReplay:
     subset of blocks (blocks are independent); by default all are kept.
     """
 
-    def __init__(self, g: Geometry, blocks=None):
+    def __init__(self, g: Geometry, blocks=None, sink_gap: int = 0, rope_theta: float = 10000.0):
         self.g = g
+        self.sink_gap = sink_gap
+        self.rope_theta = rope_theta
+        self.z0_frame = 0
         self.blocks = list(range(g.n_blocks)) if blocks is None else list(blocks)
         self.index = {b: i for i, b in enumerate(self.blocks)}
         store = np.uint16 if g.dtype == "bf16" else np.float32
@@ -249,20 +337,39 @@ class MemoryReplay:
         Returns (raw slot, sum slot, frame) or None.
         """
         g = self.g
-        if t <= g.y:
-            return None
-        s = self.raw_slot(t)
-        f = self.raw_frame[s]
-        if f < 1:
-            return None
-        u = self.sum_slot(f)
-        src0 = g.raw_rows(s)[0] + g.hw
-        src1 = g.raw_rows(s)[1]
-        dst0, dst1 = g.sum_rows(u)
-        self.k[:, dst0:dst1] = self.k[:, src0:src1]
-        self.v[:, dst0:dst1] = self.v[:, src0:src1]
-        self.sum_frame[u] = f
-        return s, u, f
+        moved = None
+        if t > g.y:
+            s = self.raw_slot(t)
+            f = self.raw_frame[s]
+            if f >= 1:
+                u = self.sum_slot(f)
+                src0 = g.raw_rows(s)[0] + g.hw
+                src1 = g.raw_rows(s)[1]
+                dst0, dst1 = g.sum_rows(u)
+                self.k[:, dst0:dst1] = self.k[:, src0:src1]
+                self.v[:, dst0:dst1] = self.v[:, src0:src1]
+                self.sum_frame[u] = f
+                moved = (s, u, f)
+        self.sink_step()
+        return moved
+
+    def oldest_frame(self) -> int:
+        """Oldest generated frame held in a RAW or SUM slot (-1: none)."""
+        held = [f for f in self.raw_frame + self.sum_frame if f >= 1]
+        return min(held) if held else -1
+
+    def sink_step(self) -> int:
+        """[sink] After an eviction step: rotate every block's Z0 keys forward when
+        the gap has reached sink_gap; returns the shift (0: none).  The rotation is
+        computed in fp64 from the stored keys and rounded once to the storage type."""
+        T = sink_shift(self.oldest_frame(), self.z0_frame, self.sink_gap)
+        if T > 0:
+            g = self.g
+            lo, hi = g.z0_rows()
+            k = stored_to_f64(self.k[:, lo:hi])
+            self.k[:, lo:hi] = f64_to_storage(rotate_temporal(k, g.head_dim, T, self.rope_theta), g.dtype)
+            self.z0_frame += T
+        return T
 
     # -- record write ([buffer]; rewrite: [sampling]) ----------------------
     def write(self, block: int, t: int, k: np.ndarray, v: np.ndarray):

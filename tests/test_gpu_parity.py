@@ -241,6 +241,7 @@ def _oracle_after(orc: so.MemoryReplay, t: int, block: int, k, v) -> so.MemoryRe
     tmp.raw_frame = list(orc.raw_frame)
     tmp.sum_frame = list(orc.sum_frame)
     tmp.t = orc.t
+    tmp.sink_gap, tmp.rope_theta, tmp.z0_frame = orc.sink_gap, orc.rope_theta, orc.z0_frame
     tmp.step(t, {block: (k, v)})
     return tmp
 

@@ -96,6 +96,7 @@ def test_buffer_sizes_and_offsets():
     (dict(hw=0), sf.SF_E_ARG), (dict(x=0), sf.SF_E_ARG), (dict(y=-1), sf.SF_E_ARG), (dict(w=2), sf.SF_E_ARG),
     (dict(n_heads=0), sf.SF_E_ARG), (dict(n_blocks=0), sf.SF_E_ARG), (dict(dtype=7), sf.SF_E_ARG),
     (dict(head_dim=96), sf.SF_E_UNSUPPORTED), (dict(max_frames=-1), sf.SF_E_ARG),
+    (dict(sink_gap=1), sf.SF_E_ARG), (dict(sink_gap=-2), sf.SF_E_ARG), (dict(sink_gap=5, rope_theta=1.0), sf.SF_E_ARG),
 ])
 def test_config_errors(bad, code):
     wl = dict(GEOMS["tiny"])
@@ -252,3 +253,23 @@ def test_tracing_on_dry_handles():
     times = sf.sf_kernel_times_read(s.handle)
     assert all(ms == 0.0 and n == 0 for ms, n in times.values())
     assert set(times) == set(sf.KERNEL_KINDS)
+
+
+@pytest.mark.parametrize("name,gap", [("tiny", 5), ("odd", 3), ("y0", 5), ("tiny", 0)])
+def test_sink_schedule_matches_oracle(name, gap):
+    """[sink]: the frame Z0's keys are rotated to, in the plan and in a dry session
+    stepped frame by frame, follows the oracle's replay (no device work)."""
+    wl = dict(GEOMS[name], sink_gap=gap)
+    cfg = sf.make_config(**wl)
+    g = so.Geometry.from_workload(wl)
+    m = so.MemoryReplay(g, blocks=[0], sink_gap=gap)
+    one = np.zeros((g.r, g.n_heads, g.head_dim), np.float32)
+    s = sf.Session(cfg, dry=True)
+    moved = 0
+    for t in range(90):
+        m.step(t, {0: (one, one)})
+        advance(s, wl, t)
+        p = sf.sf_plan(cfg, t)
+        assert p["z0_frame"] == m.z0_frame == s.view()["z0_frame"], (name, t)
+        moved += m.z0_frame > 0
+    assert (moved > 0) == (gap > 0)
