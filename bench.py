@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PREFILL = 26                # frames 0..25: from frame 25 on, every read has the full 6,528 keys
 RING = 8
+SINK_GAP = 5                # Z0 follows the window: rotated when the gap reaches 5 (model card)
 
 
 def profiled_traffic(profile, source):
@@ -58,10 +59,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-sink", action="store_true", help="leave Z0's keys where they are (no streaming sink)")
     return ap.parse_args()
 
 
-def cpu_baseline(wl, target_s):
+def cpu_baseline(wl, target_s, sink_gap):
     """Times the oracle (fp64, numpy) on served block-steps at 6,528 keys; frames/s extrapolated to 28 blocks."""
     import numpy as np
     import sf_inputs
@@ -73,7 +75,7 @@ def cpu_baseline(wl, target_s):
         threads = os.cpu_count() or 1
     one = dict(wl, n_blocks=1)
     g = so.Geometry.from_workload(one)
-    orc = so.MemoryReplay(g)
+    orc = so.MemoryReplay(g, sink_gap=sink_gap)
     for t in range(PREFILL):
         _, k, v = sf_inputs.frame_tensors(one, 0, 0, t)
         orc.step(t, {0: (sf_inputs.to_host_bytes(k), sf_inputs.to_host_bytes(v))})
@@ -116,7 +118,8 @@ def main():
 
     wl = sf_inputs.WORKLOADS["rollout"]
     nb, R, H, D, X = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"], wl["x"]
-    cfg = sf.make_config(**wl)
+    sink_gap = 0 if args.no_sink else SINK_GAP
+    cfg = sf.make_config(**wl, sink_gap=sink_gap)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -195,6 +198,8 @@ def main():
     row_bytes = H * D * 2
     evict_bytes = nb * 2 * 2 * X * row_bytes   # K and V, read + write, every block
     evict_gbps = evict_bytes / (avg("evict") * 1e-3) / 1e9
+    n_t = (D - 4 * (D // 6)) // 2                  # temporal RoPE planes per head
+    sink_bytes = nb * R * H * (2 * n_t) * 2 * 2    # Z0 keys' temporal dims, read + write, every block
     frames_per_s = args.steps / (total_ms * 1e-3)
 
     result = {
@@ -212,8 +217,11 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, bf16, resident in HBM)",
         "config": {"workload": "served rollout, steady state: 28 blocks, 16 heads x 64, 24x42 raw + 96 summary "
                                "tokens per record, Y=2, W=24, 6528 keys per read; step = eviction + 28 x "
-                               "sf_step (record write fused into the attention launch)",
-                   "blocks": nb, "heads": H, "head_dim": D, "record_rows": R, "keys": n_keys},
+                               "sf_step (record write fused into the attention launch)" +
+                               (f"; Z0 keys rotated forward when the gap reaches {sink_gap} (every "
+                                f"{sink_gap - 1} frames)" if sink_gap else ""),
+                   "blocks": nb, "heads": H, "head_dim": D, "record_rows": R, "keys": n_keys,
+                   "sink_gap": sink_gap},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("profiles/attn_sk_kernel.served_rollout.txt",
@@ -228,12 +236,15 @@ def main():
         "evict_frac_hbm": round(evict_gbps / PEAK_HBM_GBPS, 4),
         "evict_avg_us": round(avg("evict") * 1e3, 3),
         "tail_avg_us": round(avg("tail") * 1e3, 3),
+        "sink_launches": kt["sink"][1],
+        "sink_avg_us": round(avg("sink") * 1e3, 3),
+        "sink_gbps": round(sink_bytes / (avg("sink") * 1e-3) / 1e9, 1) if kt["sink"][1] else None,
         "separate_write_launches": kt["write"][1],   # 0: the attention launch writes the record
         "traced_ms_per_step": round(traced_ms / args.steps, 4),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, sink_gap)
     print(json.dumps(result), flush=True)
 
 
