@@ -35,6 +35,7 @@ EXPORTED = (
     "sf_config_check", "sf_buffer_bytes", "sf_kv_bytes", "sf_kv_offset", "sf_buffer_create",
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
+    "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import",
 )
 SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_KINDS = range(8)
 KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink")
@@ -80,6 +81,11 @@ _sig = {
     "sf_debug_fail_next_launch": (ctypes.c_int, [_P]),
     "sf_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "sf_kernel_times_read": (ctypes.c_int, [_P, ctypes.POINTER(sf_kernel_times)]),
+    "sf_record_slot": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+    "sf_commit_record": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64]),
+    "sf_state_bytes": (ctypes.c_size_t, [_CFG]),
+    "sf_state_export": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
+    "sf_state_import": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -232,6 +238,33 @@ def sf_kernel_times_read(handle: int) -> dict:
     return {KERNEL_KINDS[k]: (t.ms[k], t.launches[k]) for k in range(SF_K_KINDS)}
 
 
+def sf_record_slot(handle: int, block: int, t: int):
+    """(k_rows, v_rows) device addresses where record t of a block goes (0 on a dry handle)."""
+    k, v = _P(), _P()
+    _check(_lib.sf_record_slot(handle, block, t, ctypes.byref(k), ctypes.byref(v)), handle)
+    return k.value or 0, v.value or 0
+
+
+def sf_commit_record(handle: int, block: int, t: int) -> None:
+    _check(_lib.sf_commit_record(handle, block, t), handle)
+
+
+def sf_state_bytes(cfg: sf_config) -> int:
+    return _lib.sf_state_bytes(ctypes.byref(cfg))
+
+
+def sf_state_export(handle: int, cfg: sf_config) -> bytes:
+    n = sf_state_bytes(cfg)
+    buf = ctypes.create_string_buffer(n)
+    _check(_lib.sf_state_export(handle, buf, n), handle)
+    return buf.raw
+
+
+def sf_state_import(handle: int, data: bytes) -> None:
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    _check(_lib.sf_state_import(handle, buf, len(data)), handle)
+
+
 # ------------------------------------------------------- a session on torch
 class Session:
     """One session's memory: a torch uint8 device tensor of sf_buffer_bytes plus its handle.
@@ -315,6 +348,27 @@ class Session:
 
     def view(self) -> dict:
         return sf_query(self.handle, self.cfg)
+
+    def record_slot(self, block, t):
+        """(K, V) rows where record t of a block goes, as [R][H][d] views of the session memory."""
+        import torch
+        ka, va = sf_record_slot(self.handle, block, t)
+        dt = torch.bfloat16 if self.cfg.dtype == SF_BF16 else torch.float32
+        eb = 2 if self.cfg.dtype == SF_BF16 else 4
+        n = self.rows * self.cfg.n_heads * self.cfg.head_dim * eb
+        base = self.mem.data_ptr()
+        shape = (self.rows, self.cfg.n_heads, self.cfg.head_dim)
+        return (self.mem[ka - base:ka - base + n].view(dt).view(shape),
+                self.mem[va - base:va - base + n].view(dt).view(shape))
+
+    def commit_record(self, block, t):
+        sf_commit_record(self.handle, block, t)
+
+    def export_state(self) -> bytes:
+        return sf_state_export(self.handle, self.cfg)
+
+    def import_state(self, data: bytes):
+        sf_state_import(self.handle, data)
 
 
 def attend_batch(sessions, block, qs, outs, scale=0.0, stream=None):

@@ -692,6 +692,104 @@ sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* 
   return apply_write(buf, block, t, k, v, static_cast<hipStream_t>(hip_stream));
 }
 
+sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows, void** v_rows) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  if (!k_rows || !v_rows) return fail(buf, SF_E_ARG, "sf_record_slot: k_rows or v_rows is NULL");
+  // the same checks as a write; the pointers stand in for the caller's data
+  const char dummy = 0;
+  sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
+  if (s != SF_OK) return s;
+  if (buf->dry) {
+    *k_rows = *v_rows = nullptr;
+    return SF_OK;
+  }
+  const int64_t row_bytes = buf->geo.row_elems * elem_bytes(buf->cfg.dtype);
+  char* kb = buf->mem + block * buf->geo.block_stride + record_row0(buf, t) * row_bytes;
+  *k_rows = kb;
+  *v_rows = kb + buf->geo.tensor_bytes;
+  return SF_OK;
+}
+
+sf_status sf_commit_record(sf_buffer* buf, int32_t block, int64_t t) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  const char dummy = 0;
+  sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
+  if (s != SF_OK) return s;
+  write_state(buf, block, t);
+  return SF_OK;
+}
+
+// Host state layout: magic, version, the config, then int64 t_cur, evicted_for, z0_frame,
+// raw_frame[y+1], sum_frame[w-y], written_at[n_blocks].
+static const uint32_t kStateMagic = 0x31534653u;  // "SFS1"
+
+size_t sf_state_bytes(const sf_config* cfg) {
+  std::string why;
+  if (check_config(cfg, &why) != SF_OK) return 0;
+  return 8 + sizeof(sf_config) + 8 * (3 + (size_t)(cfg->y + 1) + (size_t)(cfg->w - cfg->y) + (size_t)cfg->n_blocks);
+}
+
+sf_status sf_state_export(const sf_buffer* buf, void* dst, size_t bytes) {
+  if (!buf || !dst) return fail(nullptr, SF_E_ARG, "sf_state_export: NULL argument");
+  const size_t need = sf_state_bytes(&buf->cfg);
+  if (bytes < need) return fail(nullptr, SF_E_ARG, "sf_state_export: destination smaller than sf_state_bytes");
+  char* p = static_cast<char*>(dst);
+  const uint32_t head[2] = {kStateMagic, 1u};
+  std::memcpy(p, head, 8);
+  p += 8;
+  std::memcpy(p, &buf->cfg, sizeof(sf_config));
+  p += sizeof(sf_config);
+  auto put = [&](int64_t x) { std::memcpy(p, &x, 8); p += 8; };
+  put(buf->slots.t_cur);
+  put(buf->slots.evicted_for);
+  put(buf->slots.z0_frame);
+  for (int64_t f : buf->slots.raw_frame) put(f);
+  for (int64_t f : buf->slots.sum_frame) put(f);
+  for (int64_t f : buf->written_at) put(f);
+  return SF_OK;
+}
+
+sf_status sf_state_import(sf_buffer* buf, const void* src, size_t bytes) {
+  if (!buf || !src) return fail(nullptr, SF_E_ARG, "sf_state_import: NULL argument");
+  const sf_config& c = buf->cfg;
+  if (bytes < sf_state_bytes(&c)) return fail(buf, SF_E_ARG, "sf_state_import: fewer bytes than sf_state_bytes");
+  const char* p = static_cast<const char*>(src);
+  uint32_t head[2];
+  std::memcpy(head, p, 8);
+  p += 8;
+  if (head[0] != kStateMagic || head[1] != 1u) return fail(buf, SF_E_ARG, "sf_state_import: not a state record");
+  if (std::memcmp(p, &c, sizeof(sf_config)) != 0)
+    return fail(buf, SF_E_ARG, "sf_state_import: the state belongs to another config");
+  p += sizeof(sf_config);
+  auto get = [&]() { int64_t x; std::memcpy(&x, p, 8); p += 8; return x; };
+  Slots s;
+  s.t_cur = get();
+  s.evicted_for = get();
+  s.z0_frame = get();
+  s.raw_frame.resize(c.y + 1);
+  s.sum_frame.resize(c.w - c.y);
+  for (auto& f : s.raw_frame) f = get();
+  for (auto& f : s.sum_frame) f = get();
+  std::vector<int64_t> wa(c.n_blocks);
+  for (auto& f : wa) f = get();
+  // consistency: every slot holds a frame it can hold at t_cur
+  bool ok = s.t_cur >= -1 && (c.max_frames == 0 || s.t_cur < c.max_frames) && s.evicted_for <= s.t_cur + 1 &&
+            s.z0_frame >= 0 && s.z0_frame <= (s.t_cur > 0 ? s.t_cur : 0);
+  for (int i = 0; i <= c.y && ok; ++i) {
+    const int64_t f = s.raw_frame[i];
+    ok = f == -1 || (f >= 1 && f <= s.t_cur && f % (c.y + 1) == i && f > s.t_cur - (c.y + 1));
+  }
+  for (int u = 0; u < c.w - c.y && ok; ++u) {
+    const int64_t f = s.sum_frame[u];
+    ok = f == -1 || (f >= 1 && f % (c.w - c.y) == u && f <= s.t_cur - (c.y + 1) + (s.evicted_for > s.t_cur));
+  }
+  for (int64_t f : wa) ok = ok && f >= -1 && f <= s.t_cur && (s.t_cur < 0 || f >= s.t_cur - 1);
+  if (!ok) return fail(buf, SF_E_ARG, "sf_state_import: inconsistent state");
+  buf->slots = s;
+  buf->written_at = wa;
+  return SF_OK;
+}
+
 sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   EvictPlan p;

@@ -147,6 +147,30 @@ sf_status sf_buffer_destroy(sf_buffer* buf);
 sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* k, const void* v,
                           void* hip_stream);
 
+/* [buffer], [sampling] Zero-copy form of sf_write_record.  Sets *k_rows and *v_rows to the
+ * device rows where record(t) of one block is stored (Z0 for t = 0, else RAW slot
+ * t mod (y+1)), each [R][n_heads][head_dim] in the config dtype (NULL on a dry-run handle),
+ * after the same checks as sf_write_record; nothing changes.  The caller fills those rows on
+ * its own stream (its K/V projection can write there directly), then calls
+ * sf_commit_record with the same block and t.  A rewrite (t == t_cur) may be filled in place
+ * as long as no read of this block is in flight. */
+sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows, void** v_rows);
+
+/* Records that record(t) of one block now sits in the rows sf_record_slot gave (same checks
+ * as sf_write_record; no device work).  A later read of the block sees those rows as they are
+ * when the read runs on its stream. */
+sf_status sf_commit_record(sf_buffer* buf, int32_t block, int64_t t);
+
+/* Host state of a session (slot map, per-block frame, Z0's frame id), for moving a session
+ * between handles: the caller copies the device bytes itself (sf_buffer_bytes of them, or the
+ * first sf_kv_bytes for K/V alone) and the host state with these.  sf_state_bytes gives the
+ * size for a config (0 if invalid); sf_state_export writes it (SF_E_ARG if bytes is smaller);
+ * sf_state_import checks it against the handle's config and for consistency and replaces the
+ * handle's state (SF_E_ARG and no change if anything is off). */
+size_t sf_state_bytes(const sf_config* cfg);
+sf_status sf_state_export(const sf_buffer* buf, void* dst, size_t bytes);
+sf_status sf_state_import(sf_buffer* buf, const void* src, size_t bytes);
+
 /* [buffer] eviction paragraph.  Before frame t is written: copies K and V of the x summary rows
  * (record rows [hw, R)) of the frame leaving RAW slot t mod (y+1) into its SUM slot
  * f mod (w-y), in every block, in one launch.  The raw rows are not copied.  t must be

@@ -33,6 +33,9 @@ WORKLOADS = {
     "served1": dict(hw=1008, x=96, y=2, w=24, n_heads=16, head_dim=64,
                     n_blocks=1, dtype="bf16", frames=list(range(32)), seed=1,
                     v_scale=1.0),
+    # the server's default window (W = 16), served grid, two blocks, 40 frames.
+    "served16": dict(hw=1008, x=96, y=2, w=16, n_heads=16, head_dim=64,
+                     n_blocks=2, dtype="bf16", frames=list(range(40)), seed=5, v_scale=1.0),
     # served grid through 28 blocks for 64 frames.
     "rollout": dict(hw=1008, x=96, y=2, w=24, n_heads=16, head_dim=64,
                     n_blocks=28, dtype="bf16", frames=list(range(64)), seed=2,

@@ -7,6 +7,8 @@ and inference code", section "One buffer, no mask".
 import os
 import re
 
+import ctypes
+
 import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
@@ -46,6 +48,7 @@ GEOMS = {
     "long": sf_inputs.WORKLOADS["long"],
     "odd": dict(hw=5, x=3, y=1, w=4, n_heads=2, head_dim=64, n_blocks=3, dtype="bf16"),
     "y0": dict(hw=7, x=2, y=0, w=3, n_heads=1, head_dim=128, n_blocks=2, dtype="f32"),
+    "served16": sf_inputs.WORKLOADS["served16"],
 }
 
 
@@ -273,3 +276,78 @@ def test_sink_schedule_matches_oracle(name, gap):
         assert p["z0_frame"] == m.z0_frame == s.view()["z0_frame"], (name, t)
         moved += m.z0_frame > 0
     assert (moved > 0) == (gap > 0)
+
+
+def test_served16_key_count():
+    """The server's default window W = 16 ([buffer] parameter table): R(Y+2) + (W-Y)X keys."""
+    cfg = sf.make_config(**GEOMS["served16"])
+    assert sf.sf_plan(cfg, 40)["n_keys"] == 1104 * 4 + 14 * 96 == 5760
+
+
+def test_zero_copy_slot_rules():
+    """sf_record_slot / sf_commit_record follow the write rules and move the state like a write."""
+    s, wl = dry_session("tiny")
+    for t in range(12):
+        if t >= 1:
+            if t > wl["y"] + 1:
+                with pytest.raises(sf.SfError) as ei:   # a frame must leave RAW first
+                    sf.sf_record_slot(s.handle, 0, t)
+                assert ei.value.status == sf.SF_E_ORDER
+                with pytest.raises(sf.SfError):
+                    sf.sf_commit_record(s.handle, 0, t)
+            s.evict(t)
+        before = s.view()
+        assert sf.sf_record_slot(s.handle, 0, t) == (0, 0)   # dry handle: no device rows
+        assert s.view() == before                            # asking changes nothing
+        s.commit_record(0, t)
+        p = sf.sf_plan(s.cfg, t)
+        for key in ("t_cur", "n_keys", "segments", "raw_frame", "sum_frame"):
+            assert s.view()[key] == p[key], (t, key)
+        s.commit_record(0, t)                                # a rewrite commit
+    with pytest.raises(sf.SfError) as ei:
+        sf.sf_commit_record(s.handle, 0, 14)
+    assert ei.value.status == sf.SF_E_ORDER
+
+
+def test_four_pass_frames_evict_once():
+    """[sampling]: three denoising passes and a clean pass rewrite the same frame; the state
+    after each frame equals one write per frame."""
+    s, wl = dry_session("odd")
+    for t in range(30):
+        for _ in range(4):
+            advance(s, wl, t)
+        p = sf.sf_plan(s.cfg, t)
+        v = s.view()
+        for key in ("t_cur", "n_keys", "segments", "raw_frame", "sum_frame", "evicted_for"):
+            assert v[key] == p[key], (t, key)
+
+
+def test_state_export_import():
+    """A session's host state moves to a new handle and both continue alike; bad records fail."""
+    a, wl = dry_session("tiny", sink_gap=5)
+    for t in range(25):
+        advance(a, wl, t)
+    data = a.export_state()
+    assert len(data) == sf.sf_state_bytes(a.cfg) > 0
+    b = sf.Session(a.cfg, dry=True)
+    b.import_state(data)
+    assert b.view() == a.view()
+    for t in range(25, 40):
+        advance(a, wl, t)
+        advance(b, wl, t)
+        assert b.view() == a.view(), t
+    fresh = sf.Session(a.cfg, dry=True)
+    empty = fresh.view()
+    bad = bytearray(data)
+    bad[0] ^= 1                                              # not a state record
+    with pytest.raises(sf.SfError):
+        fresh.import_state(bytes(bad))
+    other = sf.Session(sf.make_config(**dict(wl, sink_gap=0)), dry=True)
+    with pytest.raises(sf.SfError):                          # another config
+        other.import_state(data)
+    off = 8 + ctypes.sizeof(sf.sf_config) + 3 * 8           # raw_frame[0]
+    bad = bytearray(data)
+    bad[off:off + 8] = (7).to_bytes(8, "little", signed=True)   # frame 7 cannot sit in RAW slot 0
+    with pytest.raises(sf.SfError):
+        fresh.import_state(bytes(bad))
+    assert fresh.view() == empty
