@@ -32,7 +32,8 @@ this file name its parts:
              forward to bring it back to 1, values untouched.
   [level]    section "Telling a summary from a pixel: level planes": 12
              temporal planes per head; the two slowest turn by less than half
-             a radian over 1024 frames.
+             a radian over 1024 frames; summary tokens take an exact quarter
+             turn on those two; the model refuses to build unless they are idle.
   [positions] section "The rest of the model", the "Positions" item: one
              rotary table with temporal, height and width bands, indexed in
              time by frame id, adapted from Wan2.1.
@@ -54,6 +55,15 @@ Readings where the page leaves a step open (each is listed in the design doc):
     only time that frame can change), and the rotation turns every Z0 key row
     (raw and summary rows of the start image) on all temporal planes by
     rotation(T), T = oldest - 1 - (Z0's frame id).
+  * [level] Whether a summary row's quarter turn takes the place of the time
+    angle on the two slowest planes or is added to it, the page does not say;
+    both are built (ROPE_LEVEL_REPLACE, the plainer reading, and
+    ROPE_LEVEL_ADD).  Under REPLACE those planes of Z0's summary rows hold no
+    time, so the sink leaves them; under ADD the sink's plain multiply is the
+    exact composition.  Queries take the same rotation as keys, row by row.
+    "Idle" is checked as the page states it: both planes below half a radian
+    over 1024 frames.  Only the temporal band is applied; the height and
+    width bands do not depend on the frame and stay the caller's.
 
 Pin status.  Every function below is pinned by tests/test_oracle_pins.py
 against facts the page fixes (the figure's worked example, the caption's key
@@ -283,6 +293,54 @@ def rotate_temporal(k: np.ndarray, head_dim: int, frames: float, theta: float = 
     return out
 
 
+# How the temporal band reaches the stored keys.  CALLER: the keys arrive rotated
+# and the memory never rotates at a write.  LEVEL_REPLACE / LEVEL_ADD: the memory
+# rotates each record by its frame id at the write (and a query by the current
+# frame); summary rows' two slowest planes hold the level axis of [level], the
+# quarter turn taking the place of the time angle (REPLACE) or added to it (ADD).
+ROPE_CALLER, ROPE_LEVEL_REPLACE, ROPE_LEVEL_ADD = 0, 1, 2
+IDLE_SPAN_FRAMES = 1024      # [level]: the span over which the level planes must stay idle
+IDLE_BOUND_RAD = 0.5         # [level]: "idle" = less than half a radian over that span
+
+
+def level_planes_idle(head_dim: int, theta: float = 10000.0) -> bool:
+    """[level] The construction check: the two slowest temporal planes turn by less
+    than half a radian over 1024 frames (so they carry no usable position)."""
+    w = temporal_frequencies(head_dim, theta)
+    return bool(np.all(w[-2:] * IDLE_SPAN_FRAMES < IDLE_BOUND_RAD))
+
+
+def quarter_turn(x: np.ndarray, y: np.ndarray):
+    """(x + iy) * i: the exact quarter turn of a plane."""
+    return -y, x
+
+
+def rope_record_f64(a: np.ndarray, hw: int, t: int, head_dim: int, theta: float = 10000.0,
+                    mode: int = ROPE_LEVEL_REPLACE) -> np.ndarray:
+    """[level], [positions] Record(t)'s Q or K rows ([R][H][d], fp64) with the temporal
+    band applied at frame id t.  Raw rows (r < hw): every temporal plane turned by its
+    frequency times t.  Summary rows (r >= hw): the same on all but the two slowest
+    planes; on those, REPLACE puts the exact quarter turn of the input, ADD turns by
+    the time angle and then by the quarter turn."""
+    if mode not in (ROPE_LEVEL_REPLACE, ROPE_LEVEL_ADD):
+        raise ValueError("rope_record_f64: mode must be LEVEL_REPLACE or LEVEL_ADD")
+    a = np.asarray(a, dtype=np.float64)
+    out = rotate_temporal(a, head_dim, t, theta)
+    n = temporal_planes(head_dim)
+    lv = slice(2 * (n - 2), 2 * n)
+    src = a[hw:, ..., lv] if mode == ROPE_LEVEL_REPLACE else out[hw:, ..., lv]
+    x, y = quarter_turn(src[..., 0::2].copy(), src[..., 1::2].copy())
+    out[hw:, ..., lv][..., 0::2] = x
+    out[hw:, ..., lv][..., 1::2] = y
+    return out
+
+
+def rope_record(stored: np.ndarray, hw: int, t: int, head_dim: int, dtype: str, theta: float = 10000.0,
+                mode: int = ROPE_LEVEL_REPLACE) -> np.ndarray:
+    """rope_record_f64 on storage bytes, rounded once back to the storage type."""
+    return f64_to_storage(rope_record_f64(stored_to_f64(stored), hw, t, head_dim, theta, mode), dtype)
+
+
 def sink_shift(oldest: int, z0_frame: int, gap: int) -> int:
     """[sink] Frames Z0 moves forward after an eviction step: back to a gap of 1
     once the gap to the oldest generated frame in memory reaches ``gap``."""
@@ -304,10 +362,12 @@ class MemoryReplay:
     subset of blocks (blocks are independent); by default all are kept.
     """
 
-    def __init__(self, g: Geometry, blocks=None, sink_gap: int = 0, rope_theta: float = 10000.0):
+    def __init__(self, g: Geometry, blocks=None, sink_gap: int = 0, rope_theta: float = 10000.0,
+                 rope_mode: int = ROPE_CALLER):
         self.g = g
         self.sink_gap = sink_gap
         self.rope_theta = rope_theta
+        self.rope_mode = rope_mode
         self.z0_frame = 0
         self.blocks = list(range(g.n_blocks)) if blocks is None else list(blocks)
         self.index = {b: i for i, b in enumerate(self.blocks)}
@@ -367,7 +427,12 @@ class MemoryReplay:
             g = self.g
             lo, hi = g.z0_rows()
             k = stored_to_f64(self.k[:, lo:hi])
-            self.k[:, lo:hi] = f64_to_storage(rotate_temporal(k, g.head_dim, T, self.rope_theta), g.dtype)
+            turned = f64_to_storage(rotate_temporal(k, g.head_dim, T, self.rope_theta), g.dtype)
+            if self.rope_mode == ROPE_LEVEL_REPLACE:
+                # a summary row's level planes hold a fixed quarter turn, not a time: kept
+                n = temporal_planes(g.head_dim)
+                turned[:, g.hw:, :, 2 * (n - 2):2 * n] = self.k[:, lo + g.hw:hi, :, 2 * (n - 2):2 * n]
+            self.k[:, lo:hi] = turned
             self.z0_frame += T
         return T
 
@@ -386,7 +451,10 @@ class MemoryReplay:
             lo, hi = g.raw_rows(s)
             self.raw_frame[s] = t
         i = self.index[block]
-        self.k[i, lo:hi] = np.asarray(k).reshape(g.r, g.n_heads, g.head_dim)
+        k = np.asarray(k).reshape(g.r, g.n_heads, g.head_dim)
+        if self.rope_mode != ROPE_CALLER:
+            k = rope_record(k, g.hw, t, g.head_dim, g.dtype, self.rope_theta, self.rope_mode)
+        self.k[i, lo:hi] = k
         self.v[i, lo:hi] = np.asarray(v).reshape(g.r, g.n_heads, g.head_dim)
         self.t = t
 
@@ -434,12 +502,17 @@ class MemoryReplay:
         """Frame t's record attends to every readable row of one block, fp64.
 
         q: [R][H][d] storage bytes (or fp64).  ``rows`` optionally restricts the
-        query rows computed (for sampled checks at large sizes).
+        query rows computed (for sampled checks at large sizes).  With the memory
+        applying the temporal band, q arrives unrotated and is turned as record(t)'s
+        rows are, t being the current frame, and rounded to the storage type.
         """
         g = self.g
         if scale is None or scale <= 0:
             scale = default_scale(g.head_dim)
-        qf = stored_to_f64(np.asarray(q).reshape(-1, g.n_heads, g.head_dim))
+        q = np.asarray(q).reshape(-1, g.n_heads, g.head_dim)
+        if self.rope_mode != ROPE_CALLER:
+            q = rope_record(q, g.hw, self.t, g.head_dim, g.dtype, self.rope_theta, self.rope_mode)
+        qf = stored_to_f64(q)
         if rows is not None:
             qf = qf[np.asarray(rows)]
         kf, vf = self.gathered(block)
