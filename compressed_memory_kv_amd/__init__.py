@@ -35,17 +35,19 @@ EXPORTED = (
     "sf_config_check", "sf_buffer_bytes", "sf_kv_bytes", "sf_kv_offset", "sf_buffer_create",
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
-    "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import",
+    "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import", "sf_rope_rows",
 )
-SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_KINDS = range(8)
-KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink")
+SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_ROPE, SF_K_KINDS = range(9)
+KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink", "rope")
+SF_ROPE_CALLER, SF_ROPE_LEVEL_REPLACE, SF_ROPE_LEVEL_ADD = 0, 1, 2
+ROPE_MODES = {"caller": SF_ROPE_CALLER, "replace": SF_ROPE_LEVEL_REPLACE, "add": SF_ROPE_LEVEL_ADD}
 
 
 class sf_config(ctypes.Structure):
     _fields_ = [("hw", ctypes.c_int32), ("x", ctypes.c_int32), ("y", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("max_frames", ctypes.c_int64), ("sink_gap", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("rope_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class sf_view(ctypes.Structure):
@@ -86,6 +88,7 @@ _sig = {
     "sf_state_bytes": (ctypes.c_size_t, [_CFG]),
     "sf_state_export": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "sf_state_import": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
+    "sf_rope_rows": (ctypes.c_int, [_CFG, ctypes.c_int64, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -130,10 +133,12 @@ def _stream(s) -> int | None:
 
 
 def make_config(hw, x, y, w, n_heads, head_dim, n_blocks=1, dtype="bf16", max_frames=0, sink_gap=0,
-                rope_theta=10000.0, **_ignored) -> sf_config:
-    """sf_config from keyword fields (extra keys, e.g. of a workload dict, are ignored)."""
+                rope_theta=10000.0, rope_mode="caller", **_ignored) -> sf_config:
+    """sf_config from keyword fields (extra keys, e.g. of a workload dict, are ignored).
+    rope_mode: "caller", "replace" or "add" (or the SF_ROPE_* value)."""
     return sf_config(hw, x, y, w, n_heads, head_dim, n_blocks, DTYPES[dtype] if isinstance(dtype, str) else dtype,
-                     max_frames, sink_gap, rope_theta)
+                     max_frames, sink_gap, rope_theta,
+                     ROPE_MODES[rope_mode] if isinstance(rope_mode, str) else rope_mode, 0)
 
 
 # --------------------------------------------------------------- the C calls
@@ -184,6 +189,10 @@ def sf_attend(handles, block: int, q, out, scale: float = 0.0, stream=None) -> N
 
 def sf_step(handle: int, block: int, t: int, q, k, v, out, scale: float = 0.0, stream=None) -> None:
     _check(_lib.sf_step(handle, block, t, _ptr(q), _ptr(k), _ptr(v), _ptr(out), scale, _stream(stream)), handle)
+
+
+def sf_rope_rows(cfg: sf_config, t: int, src, dst, stream=None) -> None:
+    _check(_lib.sf_rope_rows(ctypes.byref(cfg), t, _ptr(src), _ptr(dst), _stream(stream)), None)
 
 
 def _view_dict(v: sf_view, raw, summ) -> dict:

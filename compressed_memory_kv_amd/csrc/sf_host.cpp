@@ -36,8 +36,19 @@ constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 31;
 int64_t elem_bytes(int32_t dtype) { return dtype == SF_BF16 ? 2 : 4; }
 
 struct Geo {
-  int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, total;
+  int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, qrot_off, total;
 };
+
+// Dims of the temporal band of a head (Wan2.1 split: hd - 4*floor(hd/6), first in the head).
+int temporal_dims(int head_dim) { return head_dim - 4 * (head_dim / 6); }
+
+// [level] The construction check: both level planes (the two slowest temporal planes) turn
+// by less than half a radian over 1024 frames, so they carry no usable position.
+bool level_planes_idle(const sf_config& c) {
+  const int dim_t = temporal_dims(c.head_dim);
+  const int slow = dim_t / 2 - 2;  // the faster of the two
+  return std::pow((double)c.rope_theta, -2.0 * slow / dim_t) * 1024.0 < 0.5;
+}
 
 sf_status check_config(const sf_config* c, std::string* why) {
   if (!c) { *why = "config is NULL"; return SF_E_ARG; }
@@ -47,11 +58,22 @@ sf_status check_config(const sf_config* c, std::string* why) {
     return SF_E_ARG;
   }
   if (c->dtype != SF_F32 && c->dtype != SF_BF16) { *why = "dtype must be SF_F32 or SF_BF16"; return SF_E_ARG; }
-  if (c->sink_gap < 0 || c->sink_gap == 1 || (c->sink_gap > 0 && !(c->rope_theta > 1.0f))) {
-    *why = "sink_gap must be 0 (off) or >= 2, with rope_theta > 1";
+  if (c->reserved != 0) { *why = "reserved must be 0"; return SF_E_ARG; }
+  if (c->rope_mode != SF_ROPE_CALLER && c->rope_mode != SF_ROPE_LEVEL_REPLACE && c->rope_mode != SF_ROPE_LEVEL_ADD) {
+    *why = "rope_mode must be SF_ROPE_CALLER, SF_ROPE_LEVEL_REPLACE or SF_ROPE_LEVEL_ADD";
+    return SF_E_ARG;
+  }
+  if (c->sink_gap < 0 || c->sink_gap == 1 || ((c->sink_gap > 0 || c->rope_mode != SF_ROPE_CALLER) &&
+                                              !(c->rope_theta > 1.0f))) {
+    *why = "sink_gap must be 0 (off) or >= 2, and rope_theta > 1 when the sink or the rope mode uses it";
     return SF_E_ARG;
   }
   if (c->head_dim != 64 && c->head_dim != 128) { *why = "head_dim must be 64 or 128"; return SF_E_UNSUPPORTED; }
+  if (c->rope_mode != SF_ROPE_CALLER && !level_planes_idle(*c)) {
+    *why = "the two slowest temporal planes turn by 0.5 rad or more over 1024 frames at this rope_theta: "
+           "they are not idle and cannot carry the level axis";
+    return SF_E_UNSUPPORTED;
+  }
   if (c->y + 1 > 4096 || c->w - c->y > (1 << 20) || c->n_blocks > 4096 || c->n_heads > 4096) {
     *why = "config too large (y+1 <= 4096, w-y <= 2^20, n_blocks <= 4096, n_heads <= 4096)";
     return SF_E_UNSUPPORTED;
@@ -78,7 +100,10 @@ Geo geometry(const sf_config* c) {
   g.scratch_bytes = c->dtype != SF_BF16 ? 0
                     : c->head_dim == 64 ? (int64_t)sf::sk_scratch_bytes(g.R, c->n_heads, g.C)
                                         : (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim);
-  g.total = g.scratch_off + g.scratch_bytes;
+  // a rotated query (rope modes): R rows, 256-byte aligned after the scratch
+  g.qrot_off = (g.scratch_off + g.scratch_bytes + 255) / 256 * 256;
+  g.total = c->rope_mode == SF_ROPE_CALLER ? g.scratch_off + g.scratch_bytes
+                                           : g.qrot_off + g.R * g.row_elems * elem_bytes(c->dtype);
   return g;
 }
 
@@ -105,13 +130,12 @@ int64_t sink_shift(const sf_config& c, const Slots& s) {
   return oldest - 1 - s.z0_frame;
 }
 
-// [sink] Temporal planes of a head in the rotary table (Wan2.1 split: the temporal
-// band takes hd - 4*floor(hd/6) dims, first in the head) and their cosines and sines
-// for a shift of T frames.
-sf::SinkTable sink_table(const sf_config& c, int64_t T) {
+// [sink], [level] Temporal planes of a head in the rotary table and their cosines and
+// sines for a turn of T frames (fp64, stored as fp32).
+sf::SinkTable rope_table(const sf_config& c, int64_t T) {
   sf::SinkTable tab;
   std::memset(&tab, 0, sizeof(tab));
-  const int dim_t = c.head_dim - 4 * (c.head_dim / 6);
+  const int dim_t = temporal_dims(c.head_dim);
   tab.n_planes = dim_t / 2;
   for (int i = 0; i < tab.n_planes; ++i) {
     const double omega = std::pow((double)c.rope_theta, -2.0 * i / dim_t);
@@ -307,8 +331,11 @@ sf_status apply_evict(sf_buffer* b, int64_t t, const EvictPlan& p, hipStream_t s
     if (take_injected(b)) return fail(b, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
     if (!b->dry) {
       TraceScope ts(b->trace, SF_K_SINK, st);
-      hipError_t e = sf::launch_sink_rotate(b->mem, c.n_blocks, (size_t)b->geo.block_stride, (int)b->geo.R,
-                                            c.n_heads, c.head_dim, c.dtype == SF_BF16, sink_table(c, T), st);
+      // under the replace reading a summary row's level planes hold no time: kept
+      const int lvl_row0 = c.rope_mode == SF_ROPE_LEVEL_REPLACE ? c.hw : (int)b->geo.R;
+      hipError_t e = sf::launch_sink_rotate(b->mem, c.n_blocks, (size_t)b->geo.block_stride, lvl_row0,
+                                            (int)b->geo.R, c.n_heads, c.head_dim, c.dtype == SF_BF16,
+                                            rope_table(c, T), st);
       if (e != hipSuccess) return hip_fail(b, e, "sink rotation launch");
     }
     b->slots.z0_frame += T;
@@ -323,6 +350,9 @@ sf_status check_write(sf_buffer* b, int32_t block, int64_t t, const void* k, con
   if (t < 0) return fail(b, SF_E_ARG, "negative frame id");
   if (c.max_frames > 0 && t >= c.max_frames) return fail(b, SF_E_RANGE, "frame id at or beyond max_frames");
   if (!b->dry && (!k || !v)) return fail(b, SF_E_ARG, "k or v is NULL");
+  if (!b->dry && c.rope_mode != SF_ROPE_CALLER &&
+      ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u))
+    return fail(b, SF_E_ARG, "k and v must be 16-byte aligned");
   if (t == b->slots.t_cur) return SF_OK;  // rewrite of the current frame (clean pass)
   if (t != b->slots.t_cur + 1) return fail(b, SF_E_ORDER, "sf_write_record(t) needs t == t_cur or t_cur + 1");
   if (b->slots.t_cur >= 0 && !all_written(b, b->slots.t_cur))
@@ -354,8 +384,12 @@ sf_status launch_write(sf_buffer* b, int32_t block, int64_t t, const void* k, co
   const int64_t row_bytes = b->geo.row_elems * elem_bytes(b->cfg.dtype);
   char* kb = b->mem + block * b->geo.block_stride + record_row0(b, t) * row_bytes;
   char* vb = kb + b->geo.tensor_bytes;
+  const sf_config& c = b->cfg;
   TraceScope ts(b->trace, SF_K_WRITE, st);
-  hipError_t e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
+  hipError_t e = c.rope_mode == SF_ROPE_CALLER
+                     ? sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st)
+                     : sf::launch_rope_rows(kb, vb, k, v, (int)b->geo.R, c.hw, c.n_heads, c.head_dim,
+                                            c.dtype == SF_BF16, c.rope_mode, rope_table(c, t), st);
   if (e != hipSuccess) return hip_fail(b, e, "write launch");
   return SF_OK;
 }
@@ -375,6 +409,21 @@ sf_status check_attend_one(sf_buffer* b, int32_t block, bool after_write) {
   if (block < 0 || block >= b->cfg.n_blocks) return fail(b, SF_E_ARG, "block index out of range");
   if (!after_write && (b->slots.t_cur < 0 || b->written_at[block] != b->slots.t_cur))
     return fail(b, SF_E_STATE, "sf_attend: the block does not hold the current frame");
+  return SF_OK;
+}
+
+// [level] A query under a rope mode, turned by the session's current frame into the
+// session's own memory; *qs is then what the read uses.  Other sessions: *qs = q.
+sf_status stage_query(sf_buffer* b, const void* q, const void** qs, hipStream_t st) {
+  *qs = q;
+  const sf_config& c = b->cfg;
+  if (c.rope_mode == SF_ROPE_CALLER || b->dry) return SF_OK;
+  char* dst = b->mem + b->geo.qrot_off;
+  TraceScope ts(b->trace, SF_K_ROPE, st);
+  hipError_t e = sf::launch_rope_rows(dst, nullptr, q, nullptr, (int)b->geo.R, c.hw, c.n_heads, c.head_dim,
+                                      c.dtype == SF_BF16, c.rope_mode, rope_table(c, b->slots.t_cur), st);
+  if (e != hipSuccess) return hip_fail(b, e, "query rotation launch");
+  *qs = dst;
   return SF_OK;
 }
 
@@ -695,6 +744,8 @@ sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* 
 sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows, void** v_rows) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   if (!k_rows || !v_rows) return fail(buf, SF_E_ARG, "sf_record_slot: k_rows or v_rows is NULL");
+  if (buf->cfg.rope_mode != SF_ROPE_CALLER)
+    return fail(buf, SF_E_UNSUPPORTED, "sf_record_slot: rows are stored as given; not under a rope mode");
   // the same checks as a write; the pointers stand in for the caller's data
   const char dummy = 0;
   sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
@@ -712,6 +763,8 @@ sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows
 
 sf_status sf_commit_record(sf_buffer* buf, int32_t block, int64_t t) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  if (buf->cfg.rope_mode != SF_ROPE_CALLER)
+    return fail(buf, SF_E_UNSUPPORTED, "sf_commit_record: rows are stored as given; not under a rope mode");
   const char dummy = 0;
   sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
   if (s != SF_OK) return s;
@@ -818,11 +871,19 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
     sf_status s = check_attend_one(b, block, false);
     if (s != SF_OK) return fail(bufs[0], s, b->err);
     if (!dry && (!q[i] || !out[i])) return fail(bufs[0], SF_E_ARG, "sf_attend: q or out pointer is NULL");
+    if (!dry && b->cfg.rope_mode != SF_ROPE_CALLER && (reinterpret_cast<uintptr_t>(q[i]) & 15u))
+      return fail(bufs[0], SF_E_ARG, "sf_attend: q must be 16-byte aligned under a rope mode");
   }
   for (int i = 0; i < n; ++i)
     if (take_injected(bufs[i])) return fail(bufs[0], SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
   if (dry) return SF_OK;
-  return enqueue_attend(bufs, n, block, q, out, scale, static_cast<hipStream_t>(hip_stream));
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const void* qs[SF_MAX_BATCH];
+  for (int i = 0; i < n; ++i) {
+    sf_status s = stage_query(bufs[i], q[i], &qs[i], st);
+    if (s != SF_OK) return fail(bufs[0], s, bufs[i]->err);
+  }
+  return enqueue_attend(bufs, n, block, qs, out, scale, st);
 }
 
 sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k, const void* v, void* out,
@@ -830,6 +891,8 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (!buf->dry && (!q || !out)) return fail(buf, SF_E_ARG, "sf_step: q or out is NULL");
+  if (!buf->dry && buf->cfg.rope_mode != SF_ROPE_CALLER && (reinterpret_cast<uintptr_t>(q) & 15u))
+    return fail(buf, SF_E_ARG, "sf_step: q must be 16-byte aligned under a rope mode");
   if (!(scale == scale) || std::isinf(scale)) return fail(buf, SF_E_ARG, "sf_step: scale is not finite");
   // Validate every part before enqueueing anything.
   EvictPlan ep;
@@ -859,8 +922,9 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   void* outs[1] = {out};
   // bf16, head_dim 64: the attention launch writes the record itself (and reads its keys
   // from k and v) whenever the block has a full 64-key tile after the write and the rows
-  // around the record fit the remaining segment slots.
-  if (!buf->dry && buf->cfg.dtype == SF_BF16 && buf->cfg.head_dim == 64) {
+  // around the record fit the remaining segment slots.  Not under a rope mode: there the
+  // stored keys are the turned ones, written first.
+  if (!buf->dry && buf->cfg.dtype == SF_BF16 && buf->cfg.head_dim == 64 && buf->cfg.rope_mode == SF_ROPE_CALLER) {
     write_state(buf, block, t);
     Segs sg;
     readable(buf->cfg, buf->geo, buf->slots, &sg);
@@ -883,8 +947,27 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   }
   if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
   if (buf->dry) return SF_OK;
+  s = stage_query(buf, q, &qs[0], st);
+  if (s != SF_OK) return restore(s);
   s = enqueue_attend(one, 1, block, qs, outs, scale, st);
   if (s != SF_OK) return restore(s);
+  return SF_OK;
+}
+
+sf_status sf_rope_rows(const sf_config* cfg, int64_t t, const void* src, void* dst, void* hip_stream) {
+  std::string why;
+  sf_status st = check_config(cfg, &why);
+  if (st != SF_OK) return fail(nullptr, st, why);
+  if (cfg->rope_mode == SF_ROPE_CALLER) return fail(nullptr, SF_E_ARG, "sf_rope_rows: the config's rope mode turns nothing");
+  if (t < 0 || (cfg->max_frames > 0 && t >= cfg->max_frames)) return fail(nullptr, SF_E_RANGE, "sf_rope_rows: bad frame id");
+  if (!src || !dst) return fail(nullptr, SF_E_ARG, "sf_rope_rows: NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+    return fail(nullptr, SF_E_ARG, "sf_rope_rows: pointers must be 16-byte aligned");
+  const Geo g = geometry(cfg);
+  hipError_t e = sf::launch_rope_rows(dst, nullptr, src, nullptr, (int)g.R, cfg->hw, cfg->n_heads, cfg->head_dim,
+                                      cfg->dtype == SF_BF16, cfg->rope_mode, rope_table(*cfg, t),
+                                      static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(nullptr, SF_E_HIP, std::string("sf_rope_rows launch: ") + hipGetErrorString(e));
   return SF_OK;
 }
 

@@ -122,9 +122,8 @@ hipError_t launch_copy_rows(void* dst_k, void* dst_v, const void* src_k, const v
 // block b's K starts at mem + b*block_stride, its V at that + v_offset.
 hipError_t launch_evict(void* mem, int n_blocks, size_t block_stride, size_t v_offset,
                         size_t src_off, size_t dst_off, size_t bytes, hipStream_t stream);
-// Streaming sink: rotates the first n_planes (dim 2i, 2i+1) planes of every head of the
-// first `rows` K rows of every block (K of block b at mem + b*block_stride) by the
-// angle with cosine c[i] and sine s[i].
+// Rotary tables: the first n_planes (dims 2i, 2i+1) planes of a head turn by the angle
+// with cosine c[i] and sine s[i].
 constexpr int kSinkMaxPlanes = 32;
 struct SinkTable {
   int32_t n_planes;
@@ -132,8 +131,18 @@ struct SinkTable {
   float c[kSinkMaxPlanes];
   float s[kSinkMaxPlanes];
 };
-hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int rows, int heads, int head_dim,
-                              bool bf16, const SinkTable& tab, hipStream_t stream);
+// Streaming sink: turns those planes of every head of the first `rows` K rows of every
+// block (K of block b at mem + b*block_stride), in place.  Rows from lvl_row0 on keep
+// their two slowest planes.
+hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int lvl_row0, int rows, int heads,
+                              int head_dim, bool bf16, const SinkTable& tab, hipStream_t stream);
+// Rotating write: `rows` rows [heads][head_dim] from src_k to dst_k with those planes
+// turned (summary rows, from hw on, take the level planes: level_mode 1 = the quarter turn
+// of the input, 2 = turned then the quarter turn), and src_v to dst_v as they are (both
+// NULL for a query).  16-byte aligned pointers; dst may equal src.
+hipError_t launch_rope_rows(void* dst_k, void* dst_v, const void* src_k, const void* src_v, int rows, int hw,
+                            int heads, int head_dim, bool bf16, int level_mode, const SinkTable& tab,
+                            hipStream_t stream);
 hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream);

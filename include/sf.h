@@ -21,6 +21,10 @@
  *              memory reaches 5; values are untouched.  With "Telling a summary
  *              from a pixel: level planes" (12 temporal planes per head) and
  *              the "Positions" item (a rotary table adapted from Wan2.1).
+ *   [level]    "Telling a summary from a pixel: level planes": the two slowest of
+ *              a head's temporal RoPE planes turn by under half a radian over 1024
+ *              frames; summary tokens take an exact quarter turn on them, and the
+ *              model refuses to build unless they are idle.
  *
  * Terms.  A session is one player's memory: n_blocks independent buffers,
  * one per transformer block, stepped together frame by frame.  R = hw + x
@@ -36,7 +40,8 @@
  * row-major in the config's dtype (so byte offset of K_b is
  * b * 2 * C*n_heads*head_dim*elem, V_b follows K_b); after the last block
  * comes a scratch region that sf_attend uses for partial results of this
- * session.  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
+ * session (and, when the library applies the temporal band, room for one rotated
+ * query).  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
  *
  * Tensors passed per call (device pointers, row-major, contiguous):
  *   q, k, v : [R][n_heads][head_dim] in the config dtype (fp32 or bf16)
@@ -79,6 +84,23 @@ typedef enum sf_status {
 
 typedef enum sf_dtype { SF_F32 = 0, SF_BF16 = 1 } sf_dtype;
 
+/* [level], [sink] Who applies the temporal RoPE band (the first hd/2 - 2*floor(hd/6) planes
+ * of a head; plane i = dims (2i, 2i+1) as (real, imaginary), turning rope_theta^(-2i /
+ * (hd - 4*floor(hd/6))) rad per frame).
+ *   SF_ROPE_CALLER         the caller's q and k arrive rotated; the library turns nothing
+ *                          except Z0's keys in the sink (every temporal plane of every row).
+ *   SF_ROPE_LEVEL_REPLACE  the library turns each record's keys by its frame id at the
+ *   SF_ROPE_LEVEL_ADD      write, and each query by the current frame at the read; raw rows
+ *                          (record rows < hw) on every temporal plane; summary rows on all
+ *                          but the two slowest, which carry the level axis: REPLACE puts the
+ *                          exact quarter turn (x, y) -> (-y, x) of the input there, ADD turns
+ *                          by the time angle and then by the quarter turn.  The height and
+ *                          width bands stay the caller's.  Under REPLACE the sink leaves the
+ *                          level planes of Z0's summary rows alone (they hold no time).
+ *                          Config check: both level planes turn by less than 0.5 rad over
+ *                          1024 frames at rope_theta, else SF_E_UNSUPPORTED. */
+typedef enum sf_rope_mode { SF_ROPE_CALLER = 0, SF_ROPE_LEVEL_REPLACE = 1, SF_ROPE_LEVEL_ADD = 2 } sf_rope_mode;
+
 /* Shape of one session ([record], [buffer] parameter table). */
 typedef struct sf_config {
   int32_t hw;         /* raw tokens per frame: one per latent grid cell (H*W), >= 1 */
@@ -94,7 +116,10 @@ typedef struct sf_config {
                          memory is sink_gap frames past Z0's frame id, Z0's keys are rotated
                          forward to bring the gap back to 1 (the page uses 5) */
   float rope_theta;   /* [sink] base of the temporal RoPE band the stored keys carry (> 1;
-                         the page's table follows Wan2.1: 10000); read only when sink_gap > 0 */
+                         the page's table follows Wan2.1: 10000); read only when sink_gap > 0
+                         or rope_mode != SF_ROPE_CALLER */
+  int32_t rope_mode;  /* [level] sf_rope_mode */
+  int32_t reserved;   /* must be 0 */
 } sf_config;
 
 #define SF_MAX_SEGMENTS 4
@@ -143,7 +168,9 @@ sf_status sf_buffer_destroy(sf_buffer* buf);
 /* [buffer], [sampling] Copies record(t)'s K and V of one block into Z0 (t = 0) or RAW slot
  * t mod (y+1).  t must be t_cur (a rewrite: last write wins) or t_cur + 1 (an advance, allowed
  * once every block holds t_cur and the frame leaving that RAW slot has been evicted).  k and v
- * are device pointers to [R][n_heads][head_dim] in the config dtype. */
+ * are device pointers to [R][n_heads][head_dim] in the config dtype (16-byte aligned).
+ * [level] Under SF_ROPE_LEVEL_*, k arrives unrotated and is stored turned by frame id t (in
+ * fp32, rounded to the storage type) in the same launch as the copy. */
 sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* k, const void* v,
                           void* hip_stream);
 
@@ -153,7 +180,9 @@ sf_status sf_write_record(sf_buffer* buf, int32_t block, int64_t t, const void* 
  * after the same checks as sf_write_record; nothing changes.  The caller fills those rows on
  * its own stream (its K/V projection can write there directly), then calls
  * sf_commit_record with the same block and t.  A rewrite (t == t_cur) may be filled in place
- * as long as no read of this block is in flight. */
+ * as long as no read of this block is in flight.  The rows are stored as given, so under
+ * SF_ROPE_LEVEL_* (where the library turns keys at the write) both calls return
+ * SF_E_UNSUPPORTED. */
 sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows, void** v_rows);
 
 /* Records that record(t) of one block now sits in the rows sf_record_slot gave (same checks
@@ -181,7 +210,8 @@ sf_status sf_state_import(sf_buffer* buf, const void* src, size_t bytes);
  * rows, all heads; values untouched) are rotated in place by rotation(T), T = oldest - 1 - z,
  * on the temporal RoPE planes, and z advances by T.  Plane i (dims 2i, 2i+1 of a head, i below
  * hd/2 - 2*floor(hd/6)) turns by T * rope_theta^(-2i / (hd - 4*floor(hd/6))); the rotation is
- * done in fp32 and rounded to the storage type. */
+ * done in fp32 and rounded to the storage type.  Under SF_ROPE_LEVEL_REPLACE the two slowest
+ * planes of Z0's summary rows are left as they are. */
 sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
 
 /* [attends], [buffer] The dense read.  For each of n sessions (n <= SF_MAX_BATCH; equal
@@ -190,14 +220,23 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
  * scale <= 0 means 1/sqrt(head_dim).  Each session's block must hold its t_cur (SF_E_STATE
  * otherwise).  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
  * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One launch
- * (plus a combine launch when the key range is split) for the whole batch. */
+ * (plus a combine launch when the key range is split) for the whole batch.
+ * [level] A session under SF_ROPE_LEVEL_* takes q unrotated: it is turned by that session's
+ * t_cur (as sf_rope_rows does) into the session's own memory first, one launch per session. */
 sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
                     void* const* out, float scale, void* hip_stream);
 
 /* One block of one frame: sf_evict(t) if it is due and has not run, then sf_write_record,
- * then sf_attend of this session alone. */
+ * then sf_attend of this session alone (q and k unrotated under SF_ROPE_LEVEL_*). */
 sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k,
                   const void* v, void* out, float scale, void* hip_stream);
+
+/* [level], [positions] The rotation the library applies under cfg's rope mode (which must be
+ * SF_ROPE_LEVEL_REPLACE or _ADD, else SF_E_ARG), for callers that read the memory with
+ * their own attention: src [R][n_heads][head_dim] (a record's q or k rows, config dtype,
+ * 16-byte aligned device pointer) turned by frame id t into dst (same shape; dst == src
+ * turns in place; partial overlap is undefined).  One launch on the stream. */
+sf_status sf_rope_rows(const sf_config* cfg, int64_t t, const void* src, void* dst, void* hip_stream);
 
 /* Host snapshot of the slot map and fill state; no device work. */
 sf_status sf_query(const sf_buffer* buf, sf_view* view);
@@ -220,9 +259,9 @@ sf_status sf_debug_fail_next_launch(sf_buffer* buf);
  * those events, returns the summed milliseconds and launch counts per kind since the last
  * read, and starts a new period.  Kinds (ATTEND: the main attention kernel; TAIL: keys past the
  * last full 64-key tile of a bf16 head_dim-64 read; COMBINE: merging of split results; SINK:
- * the rotation of Z0's keys): */
+ * the rotation of Z0's keys; ROPE: the rotation of a query before a read): */
 enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_TAIL = 5,
-       SF_K_SINK = 6, SF_K_KINDS = 7 };
+       SF_K_SINK = 6, SF_K_ROPE = 7, SF_K_KINDS = 8 };
 typedef struct sf_kernel_times {
   double ms[SF_K_KINDS];
   int64_t launches[SF_K_KINDS];

@@ -232,7 +232,7 @@ def _oracle_after(orc: so.MemoryReplay, t: int, block: int, k, v) -> so.MemoryRe
 
     `orc` holds every checked block at frame t-1; this copies only `block`."""
     tmp = so.MemoryReplay.__new__(so.MemoryReplay)
-    tmp.g = orc.g
+    tmp.__dict__.update(orc.__dict__)     # settings and scalar state; the tables and rows are copied below
     tmp.blocks = [block]
     tmp.index = {block: 0}
     i = orc.index[block]
@@ -240,8 +240,6 @@ def _oracle_after(orc: so.MemoryReplay, t: int, block: int, k, v) -> so.MemoryRe
     tmp.v = orc.v[i:i + 1].copy()
     tmp.raw_frame = list(orc.raw_frame)
     tmp.sum_frame = list(orc.sum_frame)
-    tmp.t = orc.t
-    tmp.sink_gap, tmp.rope_theta, tmp.z0_frame = orc.sink_gap, orc.rope_theta, orc.z0_frame
     tmp.step(t, {block: (k, v)})
     return tmp
 

@@ -100,6 +100,10 @@ def test_buffer_sizes_and_offsets():
     (dict(n_heads=0), sf.SF_E_ARG), (dict(n_blocks=0), sf.SF_E_ARG), (dict(dtype=7), sf.SF_E_ARG),
     (dict(head_dim=96), sf.SF_E_UNSUPPORTED), (dict(max_frames=-1), sf.SF_E_ARG),
     (dict(sink_gap=1), sf.SF_E_ARG), (dict(sink_gap=-2), sf.SF_E_ARG), (dict(sink_gap=5, rope_theta=1.0), sf.SF_E_ARG),
+    (dict(rope_mode=3), sf.SF_E_ARG), (dict(rope_mode="replace", rope_theta=0.5), sf.SF_E_ARG),
+    # [level]: at base 1000 the two slowest planes turn 3.2 rad over 1024 frames: not idle
+    (dict(rope_mode="replace", rope_theta=1000.0), sf.SF_E_UNSUPPORTED),
+    (dict(rope_mode="add", rope_theta=2048.0 ** 1.2 * 0.999), sf.SF_E_UNSUPPORTED),
 ])
 def test_config_errors(bad, code):
     wl = dict(GEOMS["tiny"])
@@ -351,3 +355,49 @@ def test_state_export_import():
     with pytest.raises(sf.SfError):
         fresh.import_state(bytes(bad))
     assert fresh.view() == empty
+
+
+@pytest.mark.parametrize("head_dim,theta", [(64, 10000.0), (128, 10000.0), (64, 2048.0 ** 1.2 * 1.001),
+                                            (64, 1000.0), (128, 500.0)])
+def test_level_idle_check_matches_oracle(head_dim, theta):
+    """[level]: the library builds a rope-mode session exactly when the oracle's idle check passes."""
+    cfg = sf.make_config(**dict(GEOMS["tiny"], head_dim=head_dim, rope_mode="add", rope_theta=theta))
+    ok = sf.sf_buffer_bytes(cfg) > 0
+    assert ok == so.level_planes_idle(head_dim, theta)
+
+
+def test_rope_mode_sizes_and_rules():
+    """Rope modes keep the K/V layout, add room for one rotated query, refuse zero-copy writes
+    and otherwise follow the same plan as the caller mode."""
+    wl = GEOMS["served"]
+    base = sf.make_config(**wl)
+    for mode in ("replace", "add"):
+        cfg = sf.make_config(**dict(wl, rope_mode=mode))
+        assert sf.sf_kv_bytes(cfg) == sf.sf_kv_bytes(base)
+        assert sf.sf_kv_offset(cfg, 3, 1) == sf.sf_kv_offset(base, 3, 1)
+        assert sf.sf_buffer_bytes(cfg) >= sf.sf_buffer_bytes(base) + 1104 * 16 * 64 * 2
+    s, wl2 = dry_session("odd", rope_mode="replace", sink_gap=3)
+    with pytest.raises(sf.SfError) as ei:
+        sf.sf_record_slot(s.handle, 0, 0)
+    assert ei.value.status == sf.SF_E_UNSUPPORTED
+    with pytest.raises(sf.SfError) as ei:
+        sf.sf_commit_record(s.handle, 0, 0)
+    assert ei.value.status == sf.SF_E_UNSUPPORTED
+    for t in range(30):
+        advance(s, wl2, t)
+        p = sf.sf_plan(s.cfg, t)
+        v = s.view()
+        for key in ("t_cur", "n_keys", "segments", "raw_frame", "sum_frame", "z0_frame"):
+            assert v[key] == p[key], (t, key)
+    with pytest.raises(sf.SfError) as ei:           # the caller mode has nothing to turn
+        sf.sf_rope_rows(sf.make_config(**GEOMS["tiny"]), 0, 16, 16)
+    assert ei.value.status == sf.SF_E_ARG
+    cfg = sf.make_config(**dict(GEOMS["tiny"], rope_mode="add"))
+    for t, src, code in ((0, 8, sf.SF_E_ARG), (-1, 16, sf.SF_E_RANGE), (0, None, sf.SF_E_ARG)):
+        with pytest.raises(sf.SfError) as ei:       # misaligned, bad frame id, NULL: refused before any launch
+            sf.sf_rope_rows(cfg, t, src, 16)
+        assert ei.value.status == code
+    bad = sf.make_config(**GEOMS["tiny"])
+    bad.reserved = 1
+    with pytest.raises(sf.SfError):
+        sf.sf_config_check(bad)
