@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-sink", action="store_true", help="leave Z0's keys where they are (no streaming sink)")
+    ap.add_argument("--no-rope-leg", action="store_true",
+                    help="skip the second leg (the same rollout with the library applying the temporal band)")
     return ap.parse_args()
 
 
@@ -101,6 +103,69 @@ def cpu_baseline(wl, target_s, sink_gap):
         "sample": f"{n} served block-steps at 6528 keys (eviction + record copy + fp64 attention of 1104 "
                   f"query rows x 16 heads x 64), {el:.1f} s; frames/s extrapolated to 28 blocks",
         "seconds_per_block_step": per_block_step,
+    }
+
+
+def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
+    """The same served rollout with the library turning keys at the write and queries at the
+    read (level planes, `mode` reading): frames/s and the rotating kernels' durations."""
+    import ctypes
+    nb, R, H, D = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"]
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    sess = sf.Session(sf.make_config(**wl, sink_gap=sink_gap, rope_mode=mode), device=dev)
+    h = sess.handle
+    out = torch.empty((R, H, D), dtype=torch.float32, device=dev)
+    for t in range(PREFILL):
+        for b in range(nb):
+            q, k, v = sf_inputs.frame_tensors(wl, 0, b, t, device=dev)
+            sf.sf_step(h, b, t, q, k, v, out, 0.0, stream)
+    ring = [[sf_inputs.frame_tensors(wl, 0, b, PREFILL + i, device=dev) for b in range(nb)] for i in range(RING)]
+    ptrs = [[(q.data_ptr(), k.data_ptr(), v.data_ptr()) for (q, k, v) in fr] for fr in ring]
+    lib, sptr, optr = sf._lib, stream.cuda_stream, out.data_ptr()
+    t = PREFILL
+
+    def frames(n):
+        nonlocal t
+        for _ in range(n):
+            fr = ptrs[(t - PREFILL) % RING]
+            rc = 0
+            for b in range(nb):
+                rc |= lib.sf_step(h, b, t, fr[b][0], fr[b][1], fr[b][2], optr, ctypes.c_float(0.0), sptr)
+            if rc != 0:
+                raise RuntimeError("libsf call failed: " + sf.sf_last_error(h))
+            t += 1
+
+    frames(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    frames(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    sf.sf_profile_enable(h, True)
+    frames(steps)
+    kt = sf.sf_kernel_times_read(h)
+    sf.sf_profile_enable(h, False)
+    avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
+    rec_bytes = R * H * D * 2
+    write_bytes = 4 * rec_bytes            # K and V read from the caller, written to the slot
+    q_bytes = 2 * rec_bytes                # the query read and its turned copy written
+    sess.close()
+    return {
+        "rope_mode": mode,
+        "frames_per_s": round(steps / (ms * 1e-3), 2),
+        "ms_per_step": round(ms / steps, 4),
+        "write_kernel": "rope_rows_kernel<true, 12> (K turned + V copied into the RAW slot)",
+        "write_avg_us": round(avg("write") * 1e3, 3),
+        "write_gbps": round(write_bytes / (avg("write") * 1e-3) / 1e9, 1),
+        "write_frac_hbm": round(write_bytes / (avg("write") * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "query_turn_avg_us": round(avg("rope") * 1e3, 3),
+        "query_turn_gbps": round(q_bytes / (avg("rope") * 1e-3) / 1e9, 1),
+        "attend_call_us": round((kt["attend"][0] + kt["tail"][0] + kt["combine"][0]) / max(kt["attend"][1], 1) * 1e3,
+                                3),
+        "write_launches": kt["write"][1], "query_turn_launches": kt["rope"][1],
     }
 
 
@@ -243,6 +308,8 @@ def main():
         "traced_ms_per_step": round(traced_ms / args.steps, 4),
         "wall_s": round(wall, 3),
     }
+    if not args.no_rope_leg:
+        result["rope_leg"] = rope_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, sink_gap)
     print(json.dumps(result), flush=True)

@@ -185,6 +185,14 @@ __device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int
     }                                                                                     \
   }
 
+// The lane's index, computed where it is used (volatile: never hoisted or kept live
+// across the main loop, where every register counts).
+__device__ __forceinline__ int fresh_lane() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 template <bool REC>
 __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
@@ -484,8 +492,9 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     if (it + (tile1 - tile0) < it_hi) load_q(it + (tile1 - tile0));  // the next piece's Q
 
     // ---- merge the four streams (stream 0 collects), then write
+    const int mlane = fresh_lane();
     auto merge_slot = [&](const int sl) -> float* {
-      return reinterpret_cast<float*>((sl < 3 ? st_a : st_b) + (sl % 3) * MERGE_SLOT) + lane * MERGE_FLOATS;
+      return reinterpret_cast<float*>((sl < 3 ? st_a : st_b) + (sl % 3) * MERGE_SLOT) + mlane * MERGE_FLOATS;
     };
     if (stream > 0 && wave_on) {
       float* dst = merge_slot((stream - 1) * 2 + hw);
@@ -539,9 +548,10 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       const bool whole = tile0 == 0 && tile1 == nt && !has_tail;
       // piece slot of this unit: its k-th workgroup writes slot k
       const int k = w - wg_of_iter((long long)S.it_begin + (long long)u * nt, G, N);
+      const int el32 = mlane & 31, eg = mlane >> 5;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int row = qrow0 + 32 * qb + l32;
+        const int row = qrow0 + 32 * qb + el32;
         if (row >= S.rows) continue;
         const f32x16& oa = qb == 0 ? o00 : o01;
         const f32x16& ob = qb == 0 ? o10 : o11;
@@ -552,9 +562,9 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
           float* op = S.out + row * row_stride + h * D;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            *reinterpret_cast<float4*>(op + 8 * q4 + 4 * g) =
+            *reinterpret_cast<float4*>(op + 8 * q4 + 4 * eg) =
                 make_float4(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv, oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv);
-            *reinterpret_cast<float4*>(op + 32 + 8 * q4 + 4 * g) =
+            *reinterpret_cast<float4*>(op + 32 + 8 * q4 + 4 * eg) =
                 make_float4(ob[4 * q4] * inv, ob[4 * q4 + 1] * inv, ob[4 * q4 + 2] * inv, ob[4 * q4 + 3] * inv);
           }
         } else {
@@ -563,12 +573,12 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
           float* po = S.part_o + (slot * kSkRows + rin) * D;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            *reinterpret_cast<float4*>(po + 8 * q4 + 4 * g) =
+            *reinterpret_cast<float4*>(po + 8 * q4 + 4 * eg) =
                 make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
-            *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * g) =
+            *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * eg) =
                 make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
           }
-          if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mx, lt);
+          if (eg == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mx, lt);
         }
       }
     }
