@@ -150,22 +150,20 @@ def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
     sf.sf_profile_enable(h, False)
     avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
     rec_bytes = R * H * D * 2
-    write_bytes = 4 * rec_bytes            # K and V read from the caller, written to the slot
-    q_bytes = 2 * rec_bytes                # the query read and its turned copy written
+    write_bytes = 6 * rec_bytes   # K, V and Q read from the caller; K, V written to the slot, Q to the session
     sess.close()
     return {
         "rope_mode": mode,
         "frames_per_s": round(steps / (ms * 1e-3), 2),
         "ms_per_step": round(ms / steps, 4),
-        "write_kernel": "rope_rows_kernel<true, 12> (K turned + V copied into the RAW slot)",
+        "write_kernel": "rope_rows_kernel<true, 12> (K and Q turned, V copied; one launch per sf_step)",
+        "write_bytes": write_bytes,
         "write_avg_us": round(avg("write") * 1e3, 3),
         "write_gbps": round(write_bytes / (avg("write") * 1e-3) / 1e9, 1),
         "write_frac_hbm": round(write_bytes / (avg("write") * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "query_turn_avg_us": round(avg("rope") * 1e3, 3),
-        "query_turn_gbps": round(q_bytes / (avg("rope") * 1e-3) / 1e9, 1),
         "attend_call_us": round((kt["attend"][0] + kt["tail"][0] + kt["combine"][0]) / max(kt["attend"][1], 1) * 1e3,
                                 3),
-        "write_launches": kt["write"][1], "query_turn_launches": kt["rope"][1],
+        "write_launches": kt["write"][1], "separate_query_turns": kt["rope"][1],
     }
 
 

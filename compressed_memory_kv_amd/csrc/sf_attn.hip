@@ -495,9 +495,9 @@ size_t attend_scratch_bytes(int64_t rows, int n_heads, int head_dim) {
 hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream) {
   const int grid = round_up8(a.total_units);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+    launch(attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), stream, a);
   else if (a.head_dim == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+    launch(attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -513,9 +513,9 @@ hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
   if (!any) return hipSuccess;
   const dim3 grid((max_pairs + 3) / 4, a.n_sessions);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, a);
+    launch(combine_kernel<64>, grid, dim3(256), stream, a);
   else if (a.head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, a);
+    launch(combine_kernel<128>, grid, dim3(256), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -523,9 +523,9 @@ hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
 
 hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream) {
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(a.total_units), dim3(kF32Threads), 0, stream, a);
+    launch(attn_f32_kernel<64>, dim3(a.total_units), dim3(kF32Threads), stream, a);
   else if (a.head_dim == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(a.total_units), dim3(kF32Threads), 0, stream, a);
+    launch(attn_f32_kernel<128>, dim3(a.total_units), dim3(kF32Threads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -818,19 +818,19 @@ size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows) {
 
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
   if (a.n_sessions == 1 && a.s[0].rec_seg >= 0)
-    hipLaunchKernelGGL(attn_sk_kernel<true>, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+    launch(attn_sk_kernel<true>, dim3(a.n_wg), dim3(kThreads), stream, a);
   else
-    hipLaunchKernelGGL(attn_sk_kernel<false>, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+    launch(attn_sk_kernel<false>, dim3(a.n_wg), dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_tail_kernel, dim3(total_units), dim3(kTailWaves * 64), 0, stream, a, total_units);
+  launch(attn_tail_kernel, dim3(total_units), dim3(kTailWaves * 64), stream, a, total_units);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_sk_kernel, dim3(total_units * kCombSplit), dim3(kCombThreads), 0, stream, a,
+  launch(combine_sk_kernel, dim3(total_units * kCombSplit), dim3(kCombThreads), stream, a,
                      total_units);
   return hipGetLastError();
 }

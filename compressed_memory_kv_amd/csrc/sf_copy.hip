@@ -87,7 +87,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   const size_t per_launch = (size_t)1 << 30;  // vectors per launch keeps the grid well inside 2^31
   for (size_t off = 0; off < n16; off += per_launch) {
     const size_t n = n16 - off < per_launch ? n16 - off : per_launch;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, stream,
+    launch(fill_zero_kernel, dim3(blocks_for(n)), dim3(kThreads), stream,
                        reinterpret_cast<u32x4*>(p) + off, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -102,7 +102,7 @@ hipError_t launch_copy_rows(void* dst_k, void* dst_v, const void* src_k, const v
   const size_t n16 = bytes / 16;
   const unsigned per = blocks_for(n16);
   if ((size_t)per * 2 >= ((size_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_pair_kernel, dim3(per * 2), dim3(kThreads), 0, stream, reinterpret_cast<u32x4*>(dst_k),
+  launch(copy_pair_kernel, dim3(per * 2), dim3(kThreads), stream, reinterpret_cast<u32x4*>(dst_k),
                      reinterpret_cast<u32x4*>(dst_v), reinterpret_cast<const u32x4*>(src_k),
                      reinterpret_cast<const u32x4*>(src_v), n16, per);
   return hipGetLastError();
@@ -116,7 +116,7 @@ hipError_t launch_evict(void* mem, int n_blocks, size_t block_stride, size_t v_o
   const unsigned per = blocks_for(n16);
   const size_t grid = (size_t)per * 2 * (size_t)n_blocks;
   if (grid >= ((size_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(evict_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, reinterpret_cast<char*>(mem),
+  launch(evict_kernel, dim3((unsigned)grid), dim3(kThreads), stream, reinterpret_cast<char*>(mem),
                      block_stride, v_offset, src_off, dst_off, n16, per);
   return hipGetLastError();
 }

@@ -29,6 +29,16 @@
 namespace {
 
 thread_local std::string g_thread_error;
+}  // namespace
+
+namespace sf {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev = {nullptr, nullptr, 0};
+  return ev;
+}
+}  // namespace sf
+
+namespace {
 
 constexpr int64_t kMaxRowsPerBuffer = (int64_t)1 << 30;
 constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 31;
@@ -226,24 +236,42 @@ struct sf_buffer {
 
 namespace {
 
-// Brackets one launch with events when tracing is on.
+// Times one launch when tracing is on.  By default the launch stamps the two events
+// itself (the dispatch's own start and end); `record_around` records them on the stream
+// around the enclosed launches instead (for a call that makes several).
 struct TraceScope {
   Tracer& t;
   int kind;
   hipStream_t st;
+  bool around;
   hipEvent_t a = nullptr, b = nullptr;
-  TraceScope(Tracer& tr, int k, hipStream_t s) : t(tr), kind(k), st(s) {
+  TraceScope(Tracer& tr, int k, hipStream_t s, bool record_around = false)
+      : t(tr), kind(k), st(s), around(record_around) {
     if (!t.on) return;
     a = t.get();
     b = t.get();
-    if (a && b && hipEventRecord(a, st) == hipSuccess) return;
+    if (a && b) {
+      if (!around) {
+        sf::launch_events() = {a, b, 0};
+        return;
+      }
+      if (hipEventRecord(a, st) == hipSuccess) return;
+    }
     if (a) t.free_events.push_back(a);
     if (b) t.free_events.push_back(b);
     a = b = nullptr;
   }
   ~TraceScope() {
     if (!t.on || !a || !b) return;
-    if (hipEventRecord(b, st) == hipSuccess) {
+    bool ok;
+    if (around) {
+      ok = hipEventRecord(b, st) == hipSuccess;
+    } else {
+      sf::LaunchEvents& ev = sf::launch_events();
+      ok = ev.launched == 1;  // exactly one dispatch stamped both events
+      ev = {nullptr, nullptr, 0};
+    }
+    if (ok) {
       t.pending.push_back({kind, {a, b}});
     } else {
       t.free_events.push_back(a);
@@ -380,16 +408,23 @@ void write_state(sf_buffer* b, int32_t block, int64_t t) {
   b->written_at[block] = t;
 }
 
-sf_status launch_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st) {
+// The record write.  Under a rope mode, `q` (if not NULL) is turned in the same launch
+// into the session's query rows (sf_step: the query belongs to the frame just written).
+sf_status launch_write(sf_buffer* b, int32_t block, int64_t t, const void* k, const void* v, hipStream_t st,
+                       const void* q = nullptr) {
   const int64_t row_bytes = b->geo.row_elems * elem_bytes(b->cfg.dtype);
   char* kb = b->mem + block * b->geo.block_stride + record_row0(b, t) * row_bytes;
   char* vb = kb + b->geo.tensor_bytes;
   const sf_config& c = b->cfg;
   TraceScope ts(b->trace, SF_K_WRITE, st);
-  hipError_t e = c.rope_mode == SF_ROPE_CALLER
-                     ? sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st)
-                     : sf::launch_rope_rows(kb, vb, k, v, (int)b->geo.R, c.hw, c.n_heads, c.head_dim,
-                                            c.dtype == SF_BF16, c.rope_mode, rope_table(c, t), st);
+  hipError_t e;
+  if (c.rope_mode == SF_ROPE_CALLER) {
+    e = sf::launch_copy_rows(kb, vb, k, v, (size_t)(b->geo.R * row_bytes), st);
+  } else {
+    const sf::RopeJob job = {kb, vb, q ? b->mem + b->geo.qrot_off : nullptr, k, v, q};
+    e = sf::launch_rope_rows(job, (int)b->geo.R, c.hw, c.n_heads, c.head_dim, c.dtype == SF_BF16, c.rope_mode,
+                             rope_table(c, t), st);
+  }
   if (e != hipSuccess) return hip_fail(b, e, "write launch");
   return SF_OK;
 }
@@ -420,8 +455,9 @@ sf_status stage_query(sf_buffer* b, const void* q, const void** qs, hipStream_t 
   if (c.rope_mode == SF_ROPE_CALLER || b->dry) return SF_OK;
   char* dst = b->mem + b->geo.qrot_off;
   TraceScope ts(b->trace, SF_K_ROPE, st);
-  hipError_t e = sf::launch_rope_rows(dst, nullptr, q, nullptr, (int)b->geo.R, c.hw, c.n_heads, c.head_dim,
-                                      c.dtype == SF_BF16, c.rope_mode, rope_table(c, b->slots.t_cur), st);
+  const sf::RopeJob job = {nullptr, nullptr, dst, nullptr, nullptr, q};
+  hipError_t e = sf::launch_rope_rows(job, (int)b->geo.R, c.hw, c.n_heads, c.head_dim, c.dtype == SF_BF16,
+                                      c.rope_mode, rope_table(c, b->slots.t_cur), st);
   if (e != hipSuccess) return hip_fail(b, e, "query rotation launch");
   *qs = dst;
   return SF_OK;
@@ -941,14 +977,19 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
     if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
     s = launch_write(buf, block, t, k, v, st);
     if (s != SF_OK) return restore(s);
+  } else if (!buf->dry && buf->cfg.rope_mode != SF_ROPE_CALLER) {
+    // the frame's query is turned in the write's launch
+    if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
+    write_state(buf, block, t);
+    s = launch_write(buf, block, t, k, v, st, q);
+    if (s != SF_OK) return restore(s);
+    qs[0] = buf->mem + buf->geo.qrot_off;
   } else {
     s = apply_write(buf, block, t, k, v, st);
     if (s != SF_OK) return restore(s);
   }
   if (take_injected(buf)) return restore(fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)"));
   if (buf->dry) return SF_OK;
-  s = stage_query(buf, q, &qs[0], st);
-  if (s != SF_OK) return restore(s);
   s = enqueue_attend(one, 1, block, qs, outs, scale, st);
   if (s != SF_OK) return restore(s);
   return SF_OK;
@@ -964,9 +1005,9 @@ sf_status sf_rope_rows(const sf_config* cfg, int64_t t, const void* src, void* d
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
     return fail(nullptr, SF_E_ARG, "sf_rope_rows: pointers must be 16-byte aligned");
   const Geo g = geometry(cfg);
-  hipError_t e = sf::launch_rope_rows(dst, nullptr, src, nullptr, (int)g.R, cfg->hw, cfg->n_heads, cfg->head_dim,
-                                      cfg->dtype == SF_BF16, cfg->rope_mode, rope_table(*cfg, t),
-                                      static_cast<hipStream_t>(hip_stream));
+  const sf::RopeJob job = {nullptr, nullptr, dst, nullptr, nullptr, src};
+  hipError_t e = sf::launch_rope_rows(job, (int)g.R, cfg->hw, cfg->n_heads, cfg->head_dim, cfg->dtype == SF_BF16,
+                                      cfg->rope_mode, rope_table(*cfg, t), static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(nullptr, SF_E_HIP, std::string("sf_rope_rows launch: ") + hipGetErrorString(e));
   return SF_OK;
 }

@@ -1,7 +1,8 @@
 // Private interface between the host state machine (sf_host.cpp) and the
-// gfx950 kernels (sf_copy.hip, sf_attn_bf16.hip, sf_attn_f32.hip).
+// gfx950 kernels (sf_copy.hip, sf_rope.hip, sf_attn.hip, sf_attn_sk.hip).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -18,6 +19,24 @@ namespace sf {
 __device__ __forceinline__ unsigned tid_x() { return __builtin_amdgcn_workitem_id_x(); }
 __device__ __forceinline__ unsigned wg_x() { return __builtin_amdgcn_workgroup_id_x(); }
 __device__ __forceinline__ unsigned wg_y() { return __builtin_amdgcn_workgroup_id_y(); }
+
+// Events that the next kernel launches of this thread have the dispatch itself stamp with
+// its start and end (so they bracket the kernel alone, as a profiler's dispatch timestamps
+// do); both NULL when tracing is off.  `launched` counts the launches made meanwhile.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+  int launched;
+};
+LaunchEvents& launch_events();
+
+// Every kernel of the library is launched through here.
+template <typename F, typename... Args>
+inline void launch(F kernel, const dim3& grid, const dim3& block, hipStream_t stream, Args... args) {
+  LaunchEvents& ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  ++ev.launched;
+}
 
 // Most sessions one attention launch covers; sf_attend splits larger batches.
 constexpr int kMaxLaunchSessions = 16;
@@ -136,13 +155,21 @@ struct SinkTable {
 // their two slowest planes.
 hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int lvl_row0, int rows, int heads,
                               int head_dim, bool bf16, const SinkTable& tab, hipStream_t stream);
-// Rotating write: `rows` rows [heads][head_dim] from src_k to dst_k with those planes
-// turned (summary rows, from hw on, take the level planes: level_mode 1 = the quarter turn
-// of the input, 2 = turned then the quarter turn), and src_v to dst_v as they are (both
-// NULL for a query).  16-byte aligned pointers; dst may equal src.
-hipError_t launch_rope_rows(void* dst_k, void* dst_v, const void* src_k, const void* src_v, int rows, int hw,
-                            int heads, int head_dim, bool bf16, int level_mode, const SinkTable& tab,
-                            hipStream_t stream);
+// Rotating write: each present tensor of `rows` rows [heads][head_dim] moved from src to
+// dst; K and Q with their temporal planes turned (summary rows, from hw on, take the level
+// planes: level_mode 1 = the quarter turn of the input, 2 = turned then the quarter turn),
+// V as it is.  A tensor is absent when both its pointers are NULL.  16-byte aligned
+// pointers; a dst may equal its src.  One launch.
+struct RopeJob {
+  void* dst_k;
+  void* dst_v;
+  void* dst_q;
+  const void* src_k;
+  const void* src_v;
+  const void* src_q;
+};
+hipError_t launch_rope_rows(const RopeJob& job, int rows, int hw, int heads, int head_dim, bool bf16,
+                            int level_mode, const SinkTable& tab, hipStream_t stream);
 hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream);

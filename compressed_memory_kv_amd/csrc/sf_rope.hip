@@ -135,26 +135,33 @@ __global__ __launch_bounds__(kRopeThreads) void sink_rotate_kernel(char* __restr
   }
 }
 
-// Rotating write: `rows` rows of [heads][head_dim] from src_k to dst_k with the temporal
-// planes turned, and (if src_v) src_v to dst_v as they are.  One thread per 16-byte chunk:
-// threads [0, n) take K's chunks in order, [n, 2n) V's.  Rows from hw on are summary rows:
-// their two slowest planes take `lvl_op`.  src and dst may be the same rows (in place: each
-// thread reads its chunk before it writes it).
+// Rotating write: up to three tensors of `rows` rows [heads][head_dim], each moved from
+// src to dst, either with the temporal planes turned (a record's K, a query) or as it is
+// (a record's V).  One thread per 16-byte chunk: threads [j*n, (j+1)*n) take tensor j's
+// chunks in order.  Rows from hw on are summary rows: their two slowest planes take
+// `lvl_op`.  src and dst may be the same rows (in place: each thread reads its chunk
+// before it writes it).
+struct RopeTensors {
+  u32x4* dst[3];
+  const u32x4* src[3];
+  int turn[3];
+};
+
 template <bool BF16, int NP>
-__global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(u32x4* dst_k, u32x4* dst_v, const u32x4* src_k,
-                                                                  const u32x4* src_v, unsigned n, int hw, int heads,
-                                                                  int chunks_per_head, int lvl_op, SinkTable tab) {
+__global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(const RopeTensors r, unsigned n, int n_tensors,
+                                                                  int hw, int heads, int chunks_per_head,
+                                                                  int lvl_op, SinkTable tab) {
   constexpr int PPC = BF16 ? 4 : 2;                    // planes per 16-byte chunk
-  const unsigned idx = wg_x() * kRopeThreads + tid_x();
-  if (idx >= n) {
-    if (src_v && idx < 2 * n) dst_v[idx - n] = __builtin_nontemporal_load(src_v + (idx - n));
-    return;
-  }
+  const unsigned gidx = wg_x() * kRopeThreads + tid_x();
+  const unsigned j = gidx / n;
+  if ((int)j >= n_tensors) return;
+  const unsigned idx = gidx - j * n;
+  u32x4* dst = r.dst[j];
+  const u32x4 v = __builtin_nontemporal_load(r.src[j] + idx);
   const unsigned rh = idx / (unsigned)chunks_per_head;
   const int ch = (int)(idx - rh * (unsigned)chunks_per_head);
-  const u32x4 v = __builtin_nontemporal_load(src_k + idx);
-  if (ch * PPC >= NP) {                                // past the temporal band: as it is
-    dst_k[idx] = v;
+  if (!r.turn[j] || ch * PPC >= NP) {                  // a value tensor, or past the temporal band
+    dst[idx] = v;
     return;
   }
   unsigned w[4] = {v.x, v.y, v.z, v.w};
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(u32x4* dst_k, u
   o.y = w[1];
   o.z = w[2];
   o.w = w[3];
-  dst_k[idx] = o;
+  dst[idx] = o;
 }
 
 }  // namespace
@@ -181,41 +188,51 @@ hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int 
   char* m = static_cast<char*>(mem);
   const dim3 g((unsigned)grid, (unsigned)n_blocks), t(kRopeThreads);
   if (tab.n_planes == 12 && head_dim == 64) {
-    if (bf16) hipLaunchKernelGGL((sink_rotate_kernel<true, 12>), g, t, 0, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
-    else hipLaunchKernelGGL((sink_rotate_kernel<false, 12>), g, t, 0, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
+    if (bf16) launch((sink_rotate_kernel<true, 12>), g, t, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
+    else launch((sink_rotate_kernel<false, 12>), g, t, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
   } else if (tab.n_planes == 22 && head_dim == 128) {
-    if (bf16) hipLaunchKernelGGL((sink_rotate_kernel<true, 22>), g, t, 0, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
-    else hipLaunchKernelGGL((sink_rotate_kernel<false, 22>), g, t, 0, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
+    if (bf16) launch((sink_rotate_kernel<true, 22>), g, t, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
+    else launch((sink_rotate_kernel<false, 22>), g, t, stream, m, block_stride, lvl_row0, rows, heads, head_dim, tab);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_rope_rows(void* dst_k, void* dst_v, const void* src_k, const void* src_v, int rows, int hw,
-                            int heads, int head_dim, bool bf16, int level_mode, const SinkTable& tab,
-                            hipStream_t stream) {
-  if ((reinterpret_cast<uintptr_t>(dst_k) | reinterpret_cast<uintptr_t>(src_k) | reinterpret_cast<uintptr_t>(dst_v) |
-       reinterpret_cast<uintptr_t>(src_v)) & 15u)
-    return hipErrorInvalidValue;
-  if ((src_v == nullptr) != (dst_v == nullptr) || (level_mode != 1 && level_mode != 2)) return hipErrorInvalidValue;
+hipError_t launch_rope_rows(const RopeJob& job, int rows, int hw, int heads, int head_dim, bool bf16,
+                            int level_mode, const SinkTable& tab, hipStream_t stream) {
+  RopeTensors r;
+  int nt = 0;
+  const void* srcs[3] = {job.src_k, job.src_v, job.src_q};
+  void* dsts[3] = {job.dst_k, job.dst_v, job.dst_q};
+  for (int i = 0; i < 3; ++i) {
+    if ((srcs[i] == nullptr) != (dsts[i] == nullptr)) return hipErrorInvalidValue;
+    if (!srcs[i]) continue;
+    if ((reinterpret_cast<uintptr_t>(srcs[i]) | reinterpret_cast<uintptr_t>(dsts[i])) & 15u) return hipErrorInvalidValue;
+    r.src[nt] = static_cast<const u32x4*>(srcs[i]);
+    r.dst[nt] = static_cast<u32x4*>(dsts[i]);
+    r.turn[nt] = i != 1;
+    ++nt;
+  }
+  for (int i = nt; i < 3; ++i) {
+    r.src[i] = nullptr;
+    r.dst[i] = nullptr;
+    r.turn[i] = 0;
+  }
+  if (nt == 0 || (level_mode != 1 && level_mode != 2)) return hipErrorInvalidValue;
   const int chunks = head_dim * (bf16 ? 2 : 4) / 16;
   const long long n = (long long)rows * heads * chunks;
   if (n == 0) return hipSuccess;
-  if (2 * n >= (1LL << 31)) return hipErrorInvalidValue;
-  const long long threads = src_v ? 2 * n : n;
-  const unsigned grid = (unsigned)((threads + kRopeThreads - 1) / kRopeThreads);
+  if (3 * n >= (1LL << 31)) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((nt * n + kRopeThreads - 1) / kRopeThreads);
   const int lvl_op = level_mode == 1 ? kQuarter : kTurnQuarter;
-  u32x4* dk = static_cast<u32x4*>(dst_k);
-  u32x4* dv = static_cast<u32x4*>(dst_v);
-  const u32x4* sk = static_cast<const u32x4*>(src_k);
-  const u32x4* sv = static_cast<const u32x4*>(src_v);
+  const dim3 g(grid), t(kRopeThreads);
   if (tab.n_planes == 12 && head_dim == 64) {
-    if (bf16) hipLaunchKernelGGL((rope_rows_kernel<true, 12>), dim3(grid), dim3(kRopeThreads), 0, stream, dk, dv, sk, sv, (unsigned)n, hw, heads, chunks, lvl_op, tab);
-    else hipLaunchKernelGGL((rope_rows_kernel<false, 12>), dim3(grid), dim3(kRopeThreads), 0, stream, dk, dv, sk, sv, (unsigned)n, hw, heads, chunks, lvl_op, tab);
+    if (bf16) launch((rope_rows_kernel<true, 12>), g, t, stream, r, (unsigned)n, nt, hw, heads, chunks, lvl_op, tab);
+    else launch((rope_rows_kernel<false, 12>), g, t, stream, r, (unsigned)n, nt, hw, heads, chunks, lvl_op, tab);
   } else if (tab.n_planes == 22 && head_dim == 128) {
-    if (bf16) hipLaunchKernelGGL((rope_rows_kernel<true, 22>), dim3(grid), dim3(kRopeThreads), 0, stream, dk, dv, sk, sv, (unsigned)n, hw, heads, chunks, lvl_op, tab);
-    else hipLaunchKernelGGL((rope_rows_kernel<false, 22>), dim3(grid), dim3(kRopeThreads), 0, stream, dk, dv, sk, sv, (unsigned)n, hw, heads, chunks, lvl_op, tab);
+    if (bf16) launch((rope_rows_kernel<true, 22>), g, t, stream, r, (unsigned)n, nt, hw, heads, chunks, lvl_op, tab);
+    else launch((rope_rows_kernel<false, 22>), g, t, stream, r, (unsigned)n, nt, hw, heads, chunks, lvl_op, tab);
   } else {
     return hipErrorInvalidValue;
   }

@@ -44,3 +44,23 @@ def test_kernel_times_count_every_launch():
     assert times["write"][1] == 0
     assert times["attend"][1] == 4 and times["evict"][1] == 2
     sf.sf_profile_enable(sess.handle, False)
+
+
+@needs_gpu
+def test_rope_mode_launches():
+    """Under a rope mode sf_step turns the query in its write launch; sf_attend turns it in a
+    launch of its own."""
+    import compressed_memory_kv_amd as sf
+    wl = dict(sf_inputs.WORKLOADS["served1"], rope_mode="replace")
+    sess = sf.Session(sf.make_config(**wl))
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    sf.sf_profile_enable(sess.handle, True)
+    for t in range(4):
+        q, k, v = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
+        sess.step(0, t, q, k, v, out)
+    times = sf.sf_kernel_times_read(sess.handle)
+    assert times["write"][1] == 4 and times["rope"][1] == 0 and times["attend"][1] == 4
+    sess.attend(0, q, out)
+    times = sf.sf_kernel_times_read(sess.handle)
+    assert times["rope"][1] == 1 and times["attend"][1] == 1 and times["write"][1] == 0
+    sf.sf_profile_enable(sess.handle, False)
