@@ -188,3 +188,64 @@ def test_rope_step_equals_separate_calls():
         torch.cuda.synchronize()
         assert torch.equal(oa, ob), t
     assert torch.equal(a.kv_bytes_view(), b.kv_bytes_view())
+
+
+@needs_gpu
+def test_rope_batched_attend_mixed_modes():
+    """One batched sf_attend over sessions with different rope modes and fill levels: each
+    session's query is turned by its own current frame."""
+    base = dict(CASES["served_bf16"], n_blocks=1)
+    plan = [("replace", 2, 11), ("add", 5, 12), ("caller", 3, 13), ("add", 9, 14)]
+    sessions, oracles, qs = [], [], []
+    for mode, t_last, seed in plan:
+        wl = dict(base, rope_mode=mode, seed=seed, sink_gap=0)
+        sess = sf.Session(sf.make_config(**wl))
+        m = {"replace": so.ROPE_LEVEL_REPLACE, "add": so.ROPE_LEVEL_ADD, "caller": so.ROPE_CALLER}[mode]
+        orc = so.MemoryReplay(so.Geometry.from_workload(wl), rope_mode=m)
+        out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+        for t in range(t_last + 1):
+            q, k, v = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
+            sess.step(0, t, q, k, v, out)
+            orc.step(t, {0: (host_bits(k), host_bits(v))})
+        sessions.append(sess)
+        oracles.append(orc)
+        qs.append(q)
+        say(f"[rope batched] {mode} at t={t_last}: {orc.n_keys()} keys")
+    outs = [torch.empty(sf_inputs.record_shape(base), dtype=torch.float32, device="cuda") for _ in plan]
+    sf.sf_attend([s.handle for s in sessions], 0, qs, outs)
+    torch.cuda.synchronize()
+    for (mode, t_last, _), orc, q, out in zip(plan, oracles, qs, outs):
+        ref = orc.attend(0, host_bits(q))
+        got = out.double().cpu().numpy()
+        err = np.abs(got - ref)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        say(f"   {mode} t={t_last}: max-abs {err.max():.2e} rel-L2 {rel:.2e}")
+        assert err.max() <= TOL["bf16"]["max_abs"] and rel <= TOL["bf16"]["rel_l2"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("mode", list(MODES))
+def test_rope_four_pass_rewrites(mode):
+    """Three denoising passes and a clean pass per frame, each a write of the same frame id
+    (turned by it) and a read, with the sink on; buffers and reads against the oracle."""
+    wl = dict(CASES["tiny_f32"], rope_mode=mode, sink_gap=3, w=4)
+    g = so.Geometry.from_workload(wl)
+    sess = sf.Session(sf.make_config(**wl))
+    orc = so.MemoryReplay(g, sink_gap=3, rope_mode=MODES[mode])
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    for t in range(14):
+        for p in range(4):
+            q, k, v = sf_inputs.frame_tensors(wl, p, 0, t, device="cuda")
+            sess.step(0, t, q, k, v, out)
+            torch.cuda.synchronize()
+            if p == 0:
+                orc.step(t, {0: (host_bits(k), host_bits(v))})
+            else:
+                orc.write(0, t, host_bits(k), host_bits(v))
+            ref = orc.attend(0, host_bits(q))
+            err = float(np.abs(out.double().cpu().numpy() - ref).max())
+            assert err <= TOL["f32"]["max_abs"], (t, p, err)
+        kg, vg = sess.kv(0)
+        np.testing.assert_array_equal(host_bits(vg), orc.v[0], err_msg=f"V t={t}")
+        check_turned(host_bits(kg)[g.r:], orc.k[0][g.r:], g.head_dim, g.dtype, 0, so.ROPE_CALLER, f"t={t} records")
+    assert sess.view()["z0_frame"] == orc.z0_frame > 0
