@@ -170,12 +170,14 @@ __device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int
       VOP[2 * j + db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va_, vb_, 0, 1, 2, 3, 4, 5, 6, 7)); \
     }                                                                                     \
   }
-// Lane addresses of those operands inside a stage (K chunk c of row r at c ^ (r & 7),
-// V chunk c at c ^ 2*(r & 3): conflict-free reads).
+// Lane addresses of those operands inside a stage (K chunk c of row r at c ^ ((r >> 1) & 7),
+// V chunk c at c ^ 2*(r & 3): conflict-free reads).  A 128-byte row is half a line of the
+// 64 LDS banks, so the 16 lanes a b128 read serves per cycle (rows r .. r+15, one chunk
+// each) cover all 64 banks only if rows of the same parity differ in their swizzle: r >> 1.
 #define SK_OPERAND_ADDRESSES(BASE)                                                        \
   int kaddr[4];                                                                           \
   _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) kaddr[kk] =                            \
-      (BASE) + l32 * ROW + (((2 * kk + g) ^ (l32 & 7)) << 4);                             \
+      (BASE) + l32 * ROW + (((2 * kk + g) ^ ((l32 >> 1) & 7)) << 4);                      \
   int vaddr[2];                                                                           \
   {                                                                                       \
     const int trow_ = (lane >> 2) & 3;                                                    \
@@ -217,12 +219,14 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
 
   // A wave-wide transfer fills 1 KB = 8 rows of a stage, lane L landing at row L/8,
   // position L%8, so lane L fetches the logical chunk that belongs there (both
-  // swizzles are involutions; transfers start at multiples of 8 rows, so the chunk a
-  // lane fetches is the same for all of them).  Each wave moves its 32-row half.
+  // swizzles are involutions).  The two waves of a stream take alternate 8-row groups
+  // (wave hw: rows 8*hw + 16*m + 0..7), so every transfer of a wave starts at a row
+  // with the same (row >> 1) & 4 and the same V phase: one K chunk and one V chunk per
+  // lane for all of them.
   const int drow = lane >> 3;
-  const int kchunk = (lane & 7) ^ drow;
+  const int kchunk = (lane & 7) ^ ((hw << 2) | (drow >> 1));
   const int vchunk = (lane & 7) ^ (2 * (drow & 3));
-  const int trow0 = hw * DMA_PER_WAVE * DMA_ROWS + drow;  // tile row of transfer 0
+  const int trow0 = hw * DMA_ROWS + drow;  // tile row of transfer 0; transfer m adds 16 m
   SK_OPERAND_ADDRESSES(soff);
   const f32x16 zero16 = {};
 
@@ -291,25 +295,26 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       }
       char* kdst = st + soff + (trow0 - drow) * ROW;
       char* vdst = kdst + TILE;
+      constexpr int kStep = 2 * DMA_ROWS;  // rows between a wave's transfers
       if (kap0 + BN <= send) {
         const char* kb = (REC && sidx == kRecSlot) ? krec : kg;
         const char* vb = (REC && sidx == kRecSlot) ? vrec : vg;
         const unsigned base = (unsigned)((srow + kap0 - skey + trow0) * row_bytes);
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
-          const unsigned rb = base + (unsigned)(m * DMA_ROWS * row_bytes);
-          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          const unsigned rb = base + (unsigned)(m * kStep * row_bytes);
+          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * kStep * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * kStep * ROW), 16, 0, 0);
         }
       } else {
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
           int sg;
-          const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * DMA_ROWS, sg) * row_bytes);
+          const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * kStep, sg) * row_bytes);
           const char* kb = (REC && sg == kRecSlot) ? krec : kg;
           const char* vb = (REC && sg == kRecSlot) ? vrec : vg;
-          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * DMA_ROWS * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * DMA_ROWS * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * kStep * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * kStep * ROW), 16, 0, 0);
         }
       }
     };
@@ -616,10 +621,10 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
   seg_tables<false>(S, seg_row, seg_key);
 
   // the 64-row tile of keys key0 .. key0+63 (past the last key: its row again), wave w
-  // moving rows 16w .. 16w+15 of K and of V
+  // moving rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of K and of V (one K chunk per lane for both)
   {
     const int drow = lane >> 3;
-    const int kchunk = (lane & 7) ^ drow;
+    const int kchunk = (lane & 7) ^ (((wave & 1) << 2) | (drow >> 1));
     const int vchunk = (lane & 7) ^ (2 * (drow & 3));
     const char* kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
     const char* vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
     const char* vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int trow = 16 * wave + 8 * m;
+      const int trow = 8 * wave + 32 * m;
       const int kappa = min(key0 + trow + drow, S.n_keys - 1);
       int sg;
       const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa, sg) * row_bytes);
