@@ -38,7 +38,7 @@ this file name its parts:
              rotary table with temporal, height and width bands, indexed in
              time by frame id, adapted from Wan2.1.
 
-Readings where the page leaves a step open (each is listed in the design doc):
+Readings where the page leaves a step open:
   * Frame 0 is the start image and lives in Z0; generated frames are t >= 1.
   * RAW slot of frame t is t mod (Y+1); SUM slot of frame f is f mod (W-Y).
   * In one step, the eviction runs before the new record is written.
