@@ -35,7 +35,7 @@ template <typename F, typename... Args>
 inline void launch(F kernel, const dim3& grid, const dim3& block, hipStream_t stream, Args... args) {
   LaunchEvents& ev = launch_events();
   hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
-  ++ev.launched;
+  if (hipPeekAtLastError() == hipSuccess) ++ev.launched;  // a failed launch stamps nothing
 }
 
 // Most sessions one attention launch covers; sf_attend splits larger batches.
