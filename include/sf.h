@@ -255,9 +255,10 @@ const char* sf_last_error(const sf_buffer* buf);
 sf_status sf_debug_fail_next_launch(sf_buffer* buf);
 
 /* Kernel timing (tracing).  While enabled on a handle, every kernel the library launches
- * for it is bracketed by two HIP events on the caller's stream.  sf_kernel_times waits for
- * those events, returns the summed milliseconds and launch counts per kind since the last
- * read, and starts a new period.  Kinds (ATTEND: the main attention kernel; TAIL: keys past the
+ * for it is given two HIP events that its dispatch stamps with its own start and end (on
+ * the caller's stream, through hipExtLaunchKernelGGL), so a duration covers the kernel
+ * alone.  sf_kernel_times_read waits for those events, returns the summed milliseconds and
+ * launch counts per kind since the last read, and starts a new period.  Kinds (ATTEND: the main attention kernel; TAIL: keys past the
  * last full 64-key tile of a bf16 head_dim-64 read; COMBINE: merging of split results; SINK:
  * the rotation of Z0's keys; ROPE: the rotation of a query before a read): */
 enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_TAIL = 5,
