@@ -13,7 +13,7 @@ seeded frames' inputs while frame ids, slots and evictions advance normally.
 
 Prints one JSON line.  `value` comes from the first timed region; per-kernel
 durations come from a second timed region of the same length in which the
-library brackets each kernel it launches with HIP events on this stream.
+library has each kernel it launches stamp two HIP events (its own start and end) on this stream.
 The cpu_baseline leg times the fp64 oracle on a bounded sample (rank 0, N=1).
 """
 import argparse
@@ -243,8 +243,8 @@ def main():
     wall0 = time.perf_counter()
     total_ms = timed(args.steps)
     wall = time.perf_counter() - wall0
-    # Timed region 2: the same steps with the library's kernel tracing on (HIP events
-    # recorded on this stream around every kernel it launches).
+    # Timed region 2: the same steps with the library's kernel tracing on (every kernel it
+    # launches stamps a start and an end HIP event on this stream).
     sf.sf_profile_enable(h, True)
     traced_ms = timed(args.steps)
     kt = sf.sf_kernel_times_read(h)
