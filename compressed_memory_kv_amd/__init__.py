@@ -355,6 +355,12 @@ class Session:
         sf_step(self.handle, block, t, self._check(q), self._check(k), self._check(v), self._check(out, True),
                 scale, stream)
 
+    def rope_rows(self, t, src, dst=None, stream=None):
+        """The rotation the session's rope mode applies at frame t (in place when dst is None)."""
+        dst = src if dst is None else dst
+        sf_rope_rows(self.cfg, t, self._check(src), self._check(dst), stream)
+        return dst
+
     def view(self) -> dict:
         return sf_query(self.handle, self.cfg)
 
