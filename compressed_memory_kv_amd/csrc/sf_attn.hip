@@ -125,17 +125,22 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // LDS tile geometry: one stage holds a K tile then a V tile, BN rows of 2D bytes
-// each, as 16-byte chunks permuted within each row so that the MFMA operand
-// reads are bank-conflict free:
-//   K: chunk c of row r sits at c ^ (r & 7)      (ds_read_b128: eight lanes read
-//      eight consecutive rows at one chunk -> eight distinct 16-byte groups);
-//   V: chunk c of row r sits at c ^ 2*(r & 3)    (ds_read_b64_tr_b16: a 16-lane
-//      group reads four consecutive rows x 32 bytes -> four disjoint 32-byte groups).
+// each, as 16-byte chunks permuted within each row so that the MFMA operand reads
+// are bank-conflict free on the 64 banks (256 bytes per cycle) of gfx950's LDS:
+//   K: chunk c of row r sits at c ^ ksw(r).  A ds_read_b128 serves 16 lanes (16
+//      consecutive rows at one chunk) per cycle, which must land on 16 distinct
+//      16-byte positions of a bank line: D = 128 (a row is one line) needs r & 15;
+//      D = 64 (two rows per line) needs (r >> 1) & 7.
+//   V: chunk c of row r sits at c ^ vsw(r).  A ds_read_b64_tr_b16 pass (32 lanes:
+//      rows 4g .. 4g+3, eight 8-byte words each) must cover the line once: D = 64
+//      puts two rows in a line and takes 2 * (r & 3); D = 128 takes 4 * (r & 3).
 template <int D>
 struct Tile {
   static constexpr int ROW = 2 * D;              // bytes per row
   static constexpr int KBYTES = BN * ROW;
   static constexpr int STAGE = 2 * KBYTES;       // K tile then V tile
+  static __device__ __forceinline__ int ksw(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+  static __device__ __forceinline__ int vsw(int r) { return D == 64 ? 2 * (r & 3) : 4 * (r & 3); }
 };
 
 // Probability sums above this make the tile recompute against its true max: every
@@ -183,27 +188,28 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   }
 
   // Per-thread tile-load geometry (loop invariant).  Chunk p of this thread is row
-  // tid/CH + p*RSTEP, chunk tid%CH; rows p*RSTEP apart share (row & 7), so every
-  // chunk's global and LDS offsets are those of chunk 0 plus a constant.
+  // tid/CH + p*RSTEP, chunk tid%CH; rows p*RSTEP apart share their swizzles (both
+  // depend on row & 15 at most), so every chunk's global and LDS offsets are those
+  // of chunk 0 plus a constant.
   constexpr int RSTEP = kThreads / CH;
-  static_assert(RSTEP % 8 == 0, "chunks of one thread share their swizzle");
+  static_assert(RSTEP % 16 == 0, "chunks of one thread share their swizzle");
   const char* __restrict__ kg = U.k + 2 * U.h * D;
   const char* __restrict__ vg = U.v + 2 * U.h * D;
   const int prow = tid / CH;
   const unsigned goff = (unsigned)(prow * row_bytes + (tid % CH) * 16);
   const unsigned gstep = (unsigned)(RSTEP * row_bytes);
-  const int ksoff = prow * T::ROW + (((tid % CH) ^ (prow & 7)) << 4);
-  const int vsoff = T::KBYTES + prow * T::ROW + (((tid % CH) ^ (2 * (prow & 3))) << 4);
+  const int ksoff = prow * T::ROW + (((tid % CH) ^ T::ksw(prow)) << 4);
+  const int vsoff = T::KBYTES + prow * T::ROW + (((tid % CH) ^ T::vsw(prow)) << 4);
   // Per-lane LDS operand addresses (bytes within a stage).
   int kaddr[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = l32 * T::ROW + (((2 * kk + g) ^ (l32 & 7)) << 4);
+  for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = l32 * T::ROW + (((2 * kk + g) ^ T::ksw(l32)) << 4);
   const int trow = (lane >> 2) & 3;
   int vaddr[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
     const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    vaddr[db] = T::KBYTES + (4 * g + trow) * T::ROW + ((chunk ^ (2 * trow)) << 4) + 8 * (lane & 1);
+    vaddr[db] = T::KBYTES + (4 * g + trow) * T::ROW + ((chunk ^ T::vsw(trow)) << 4) + 8 * (lane & 1);
   }
 
   // Loads tile TILE into staging registers KR/VR.  A tile inside one segment is a
