@@ -95,7 +95,7 @@ def cpu_baseline(wl, target_s, sink_gap):
             break
     assert orc.n_keys() == 6528
     per_block_step = el / n
-    return {
+    result = {
         "value": 1.0 / (per_block_step * wl["n_blocks"]),
         "unit": "frames/s",
         "cores": int(threads),
@@ -103,7 +103,20 @@ def cpu_baseline(wl, target_s, sink_gap):
         "sample": f"{n} served block-steps at 6528 keys (eviction + record copy + fp64 attention of 1104 "
                   f"query rows x 16 heads x 64), {el:.1f} s; frames/s extrapolated to 28 blocks",
         "seconds_per_block_step": per_block_step,
+        "gflops": 4.0 * 1104 * 6528 * 16 * 64 / per_block_step / 1e9,
     }
+    # the same oracle on one core: one more block-step with the BLAS pool held to one thread
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            s1 = time.perf_counter()
+            orc.step(t, {0: (k, v)})
+            orc.attend(0, q)
+            one_core = time.perf_counter() - s1
+        result["one_core"] = {"seconds_per_block_step": one_core, "frames_per_s": 1.0 / (one_core * wl["n_blocks"])}
+    except ImportError:
+        pass
+    return result
 
 
 def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
