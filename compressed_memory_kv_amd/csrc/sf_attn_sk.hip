@@ -701,16 +701,13 @@ __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaun
   }
 }
 
-// Merges the partials of every unit that has more than one: its pieces from
-// attn_sk_kernel (slots 0 .. last - first workgroup of the unit) and its tail (last
-// slot).  One workgroup per unit; thread t owns 8 float4 of the unit's 128 x 64 output
-// (rows t/16 + 16*i, columns 4*(t%16)).  Partials are folded in one pass with a running
-// max, and each partial's loads for all 8 elements are issued together, so a unit costs
-// one global round trip per partial.
+// Combine tiling: the partials of a unit are its pieces from attn_sk_kernel (slots
+// 0 .. last - first workgroup of the unit) and its tail (last slot).  Small workgroups
+// (16 rows of a unit each, one float4 per thread) measured faster than 32- or 64-row ones.
 constexpr int kCombThreads = 256;
-constexpr int kCombRows = 32;                                   // query rows per workgroup
+constexpr int kCombRows = 16;                                   // query rows per workgroup
 constexpr int kCombSplit = kSkRows / kCombRows;                 // workgroups per unit
-constexpr int kCombPer = kCombRows * (D / 4) / kCombThreads;    // rows per thread: 2
+constexpr int kCombPer = kCombRows * (D / 4) / kCombThreads;    // rows per thread: 1
 constexpr int kCombBatch = 4;                                   // partials loaded at once
 static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kCombRows * (D / 4), "combine tiling");
 
