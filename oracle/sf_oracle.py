@@ -37,6 +37,10 @@ this file name its parts:
   [positions] section "The rest of the model", the "Positions" item: one
              rotary table with temporal, height and width bands, indexed in
              time by frame id, adapted from Wan2.1.
+  [files]    section "Files": the model's files include an optional recency
+             bias on summary keys.
+  [credits]  section "Credits": that bias follows the Recency Forcing paper,
+             which the page does not reproduce.
 
 Readings where the page leaves a step open:
   * Frame 0 is the start image and lives in Z0; generated frames are t >= 1.
@@ -64,14 +68,24 @@ Readings where the page leaves a step open:
     "Idle" is checked as the page states it: both planes below half a radian
     over 1024 frames.  Only the temporal band is applied; the height and
     width bands do not depend on the frame and stay the caller's.
+  * [files], [credits] The recency bias is read as an additive term on the
+    scaled scores (natural-log units) of summary keys that depends only on
+    the head and on the age t - f of the key's frame f: a table of W+1
+    values per head (ages 0 .. W, all a summary row can have), given by the
+    caller, since its form comes from a paper the page does not reproduce.
+    It reaches every summary row of a generated frame (in the record, in a
+    RAW slot, in a SUM slot); raw rows and the start image's rows get none.
 
 Pin status.  Every function below is pinned by tests/test_oracle_pins.py
 against facts the page fixes (the figure's worked example, the caption's key
 counts, brute-force equality with the attention-set rule, closed forms of
 softmax attention, torch's float64 SDPA over gathered rows, the 12 temporal
 planes and the half-radian bound of [level], the composition law of [sink],
-numpy's float32 conversion for the rounding).  No function here is "parity
-unpinned".
+numpy's float32 conversion for the rounding), and by
+tests/test_oracle_bias_pins.py for the recency bias (a bias of ln n equals n
+copies of those keys; a bias of -inf equals leaving them out, checked against
+the frame-level attention rule and the figure's example).  No function here is
+"parity unpinned"; the values of the recency bias table are the caller's.
 """
 from __future__ import annotations
 
@@ -181,18 +195,22 @@ def default_scale(head_dim: int) -> float:
     return 1.0 / np.sqrt(float(head_dim))
 
 
-def attention_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+def attention_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, bias=None) -> np.ndarray:
     """Exact softmax attention, every query row against every key row, per head.
 
     q: [n][H][d], k and v: [m][H][d], all fp64.  Returns [n][H][d] fp64:
-    O[i,h] = sum_j softmax_j(scale * <q[i,h], k[j,h]>) v[j,h].  No mask and
-    no causal order ([buffer]: the read is one dense, unmasked attention).
-    Subtracting the row maximum before exp leaves the exact value unchanged.
+    O[i,h] = sum_j softmax_j(scale * <q[i,h], k[j,h]> + bias[j,h]) v[j,h].  No
+    mask and no causal order ([buffer]: the read is one dense, unmasked
+    attention).  ``bias`` ([m][H], natural-log units; None = 0) is the
+    recency bias of summary keys.  Subtracting the row maximum before exp
+    leaves the exact value unchanged.
     """
     n, n_heads, _ = q.shape
     out = np.empty((n, n_heads, v.shape[2]), dtype=np.float64)
     for h in range(n_heads):
         s = (q[:, h, :] @ k[:, h, :].T) * scale
+        if bias is not None:
+            s = s + bias[None, :, h]
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         out[:, h, :] = (p @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
@@ -363,8 +381,11 @@ class MemoryReplay:
     """
 
     def __init__(self, g: Geometry, blocks=None, sink_gap: int = 0, rope_theta: float = 10000.0,
-                 rope_mode: int = ROPE_CALLER):
+                 rope_mode: int = ROPE_CALLER, recency_bias=None):
         self.g = g
+        self.recency_bias = None
+        if recency_bias is not None:
+            self.set_recency_bias(recency_bias)
         self.sink_gap = sink_gap
         self.rope_theta = rope_theta
         self.rope_mode = rope_mode
@@ -492,6 +513,48 @@ class MemoryReplay:
     def n_keys(self) -> int:
         return sum(n for _, n in self.readable_segments())
 
+    # -- recency bias on summary keys (file list of the page: recency_bias.py) --
+    def set_recency_bias(self, table):
+        """Bias table [H][W+1], natural-log units: entry [h][a] is added to head h's
+        scaled scores against the summary keys of the frame a frames older than the
+        current one (a = 0: the current frame's own record)."""
+        g = self.g
+        tab = np.asarray(table, dtype=np.float64)
+        if tab.shape != (g.n_heads, g.w + 1):
+            raise ValueError("recency bias table must be [n_heads][w + 1]")
+        self.recency_bias = tab.copy()
+
+    def row_frames(self, rows: np.ndarray):
+        """For buffer rows: the generated frame each belongs to (-1: Z0, the start
+        image) and whether it is a summary row.  Looked up in the slot tables."""
+        g = self.g
+        frame = np.full(len(rows), -1, dtype=np.int64)
+        summary = np.zeros(len(rows), dtype=bool)
+        sum0 = g.r * (g.y + 2)
+        for j, row in enumerate(np.asarray(rows).tolist()):
+            if row < g.r:
+                continue                                   # Z0: no recency
+            if row < sum0:
+                s, within = divmod(row - g.r, g.r)
+                frame[j] = self.raw_frame[s]
+                summary[j] = within >= g.hw
+            else:
+                frame[j] = self.sum_frame[(row - sum0) // g.x]
+                summary[j] = True
+        return frame, summary
+
+    def key_bias(self, rows: np.ndarray):
+        """[len(rows)][H] recency bias of these key rows (None when off): the
+        table's entry for the age t - f of a summary row's frame f, 0 for raw rows
+        and for Z0."""
+        if self.recency_bias is None:
+            return None
+        frame, summary = self.row_frames(rows)
+        bias = np.zeros((len(rows), self.g.n_heads), dtype=np.float64)
+        for j in np.nonzero(summary & (frame >= 1))[0]:
+            bias[j] = self.recency_bias[:, self.t - frame[j]]
+        return bias
+
     def gathered(self, block: int):
         """fp64 K and V of the readable rows of one block, ascending row order."""
         rows = self.readable_rows()
@@ -516,7 +579,7 @@ class MemoryReplay:
         if rows is not None:
             qf = qf[np.asarray(rows)]
         kf, vf = self.gathered(block)
-        return attention_f64(qf, kf, vf, scale)
+        return attention_f64(qf, kf, vf, scale, self.key_bias(self.readable_rows()))
 
     # -- bytes --------------------------------------------------------------
     def block_bytes(self, block: int) -> bytes:
