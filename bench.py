@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-sink", action="store_true", help="leave Z0's keys where they are (no streaming sink)")
     ap.add_argument("--no-rope-leg", action="store_true",
                     help="skip the second leg (the same rollout with the library applying the temporal band)")
+    ap.add_argument("--no-bias-leg", action="store_true",
+                    help="skip the third leg (the same rollout with a recency bias on summary keys)")
     return ap.parse_args()
 
 
@@ -119,14 +121,16 @@ def cpu_baseline(wl, target_s, sink_gap):
     return result
 
 
-def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
-    """The same served rollout with the library turning keys at the write and queries at the
-    read (level planes, `mode` reading): frames/s and the rotating kernels' durations."""
+def run_leg(sf, sf_inputs, torch, wl, steps, warmup, setup=None, **cfg_kw):
+    """The served rollout on one session of the workload's shape with extra config fields:
+    (ms of `steps` timed frames, per-kind kernel times of `steps` more frames, traced)."""
     import ctypes
     nb, R, H, D = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"]
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
-    sess = sf.Session(sf.make_config(**wl, sink_gap=sink_gap, rope_mode=mode), device=dev)
+    sess = sf.Session(sf.make_config(**dict(wl, **cfg_kw)), device=dev)
+    if setup is not None:
+        setup(sess)
     h = sess.handle
     out = torch.empty((R, H, D), dtype=torch.float32, device=dev)
     for t in range(PREFILL):
@@ -161,10 +165,18 @@ def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
     frames(steps)
     kt = sf.sf_kernel_times_read(h)
     sf.sf_profile_enable(h, False)
+    sess.close()
+    return ms, kt
+
+
+def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
+    """The same served rollout with the library turning keys at the write and queries at the
+    read (level planes, `mode` reading): frames/s and the rotating kernels' durations."""
+    R, H, D = wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"]
+    ms, kt = run_leg(sf, sf_inputs, torch, wl, steps, warmup, sink_gap=sink_gap, rope_mode=mode)
     avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
     rec_bytes = R * H * D * 2
     write_bytes = 6 * rec_bytes   # K, V and Q read from the caller; K, V written to the slot, Q to the session
-    sess.close()
     return {
         "rope_mode": mode,
         "frames_per_s": round(steps / (ms * 1e-3), 2),
@@ -177,6 +189,32 @@ def rope_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, mode="replace"):
         "attend_call_us": round((kt["attend"][0] + kt["tail"][0] + kt["combine"][0]) / max(kt["attend"][1], 1) * 1e3,
                                 3),
         "write_launches": kt["write"][1], "separate_query_turns": kt["rope"][1],
+    }
+
+
+def bias_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup):
+    """The same served rollout with a recency bias on summary keys (a seeded N(0, 0.5^2) table
+    per head and age): frames/s and the biased read's durations.  That read goes through the
+    split-key kernel, after a separate record write."""
+    R, H, D = wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"]
+    C = R * (wl["y"] + 2) + (wl["w"] - wl["y"]) * wl["x"]
+    tab = sf_inputs.bias_table(wl, 0, 0, 0.5, device="cuda").contiguous()
+    ms, kt = run_leg(sf, sf_inputs, torch, wl, steps, warmup, setup=lambda s: s.set_recency_bias(tab),
+                     sink_gap=sink_gap, recency_bias=True)
+    avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
+    flop = 4.0 * R * C * H * D
+    return {
+        "frames_per_s": round(steps / (ms * 1e-3), 2),
+        "ms_per_step": round(ms / steps, 4),
+        "attn_kernel": "attn_bf16_kernel<64, true> (split-key, per-key bias in the score FMA)",
+        "attn_avg_us": round(avg("attend") * 1e3, 3),
+        "attn_tflops": round(flop / (avg("attend") * 1e-3) / 1e12, 2),
+        "attn_frac_mfma": round(flop / (avg("attend") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "combine_avg_us": round(avg("combine") * 1e3, 3),
+        "write_avg_us": round(avg("write") * 1e3, 3),
+        "bias_rows_avg_us": round(avg("bias") * 1e3, 3),
+        "bias_rows_launches": kt["bias"][1],
+        "attend_launches": kt["attend"][1],
     }
 
 
@@ -321,6 +359,8 @@ def main():
     }
     if not args.no_rope_leg:
         result["rope_leg"] = rope_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
+    if not args.no_bias_leg:
+        result["bias_leg"] = bias_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, sink_gap)
     print(json.dumps(result), flush=True)

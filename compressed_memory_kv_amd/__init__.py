@@ -36,9 +36,11 @@ EXPORTED = (
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
     "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import", "sf_rope_rows",
+    "sf_set_recency_bias",
 )
-SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_ROPE, SF_K_KINDS = range(9)
-KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink", "rope")
+(SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_ROPE, SF_K_BIAS,
+ SF_K_KINDS) = range(10)
+KERNEL_KINDS = ("fill", "write", "evict", "attend", "combine", "tail", "sink", "rope", "bias")
 SF_ROPE_CALLER, SF_ROPE_LEVEL_REPLACE, SF_ROPE_LEVEL_ADD = 0, 1, 2
 ROPE_MODES = {"caller": SF_ROPE_CALLER, "replace": SF_ROPE_LEVEL_REPLACE, "add": SF_ROPE_LEVEL_ADD}
 
@@ -47,7 +49,7 @@ class sf_config(ctypes.Structure):
     _fields_ = [("hw", ctypes.c_int32), ("x", ctypes.c_int32), ("y", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("max_frames", ctypes.c_int64), ("sink_gap", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float), ("rope_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_float), ("rope_mode", ctypes.c_int32), ("recency_bias", ctypes.c_int32)]
 
 
 class sf_view(ctypes.Structure):
@@ -89,6 +91,7 @@ _sig = {
     "sf_state_export": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "sf_state_import": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "sf_rope_rows": (ctypes.c_int, [_CFG, ctypes.c_int64, _P, _P, _P]),
+    "sf_set_recency_bias": (ctypes.c_int, [_P, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -133,12 +136,13 @@ def _stream(s) -> int | None:
 
 
 def make_config(hw, x, y, w, n_heads, head_dim, n_blocks=1, dtype="bf16", max_frames=0, sink_gap=0,
-                rope_theta=10000.0, rope_mode="caller", **_ignored) -> sf_config:
+                rope_theta=10000.0, rope_mode="caller", recency_bias=False, **_ignored) -> sf_config:
     """sf_config from keyword fields (extra keys, e.g. of a workload dict, are ignored).
-    rope_mode: "caller", "replace" or "add" (or the SF_ROPE_* value)."""
+    rope_mode: "caller", "replace" or "add" (or the SF_ROPE_* value); recency_bias: a bias
+    table (sf_set_recency_bias) on summary keys."""
     return sf_config(hw, x, y, w, n_heads, head_dim, n_blocks, DTYPES[dtype] if isinstance(dtype, str) else dtype,
                      max_frames, sink_gap, rope_theta,
-                     ROPE_MODES[rope_mode] if isinstance(rope_mode, str) else rope_mode, 0)
+                     ROPE_MODES[rope_mode] if isinstance(rope_mode, str) else rope_mode, int(bool(recency_bias)))
 
 
 # --------------------------------------------------------------- the C calls
@@ -193,6 +197,10 @@ def sf_step(handle: int, block: int, t: int, q, k, v, out, scale: float = 0.0, s
 
 def sf_rope_rows(cfg: sf_config, t: int, src, dst, stream=None) -> None:
     _check(_lib.sf_rope_rows(ctypes.byref(cfg), t, _ptr(src), _ptr(dst), _stream(stream)), None)
+
+
+def sf_set_recency_bias(handle: int, table, stream=None) -> None:
+    _check(_lib.sf_set_recency_bias(handle, _ptr(table), _stream(stream)), handle)
 
 
 def _view_dict(v: sf_view, raw, summ) -> dict:
@@ -354,6 +362,18 @@ class Session:
     def step(self, block, t, q, k, v, out, scale=0.0, stream=None):
         sf_step(self.handle, block, t, self._check(q), self._check(k), self._check(v), self._check(out, True),
                 scale, stream)
+
+    def set_recency_bias(self, table, stream=None):
+        """The session's recency bias: a contiguous fp32 device tensor [n_heads][w + 1]."""
+        import torch
+        shape = (self.cfg.n_heads, self.cfg.w + 1)
+        if self.dry:
+            sf_set_recency_bias(self.handle, None, stream)
+            return
+        if not isinstance(table, torch.Tensor) or table.dtype != torch.float32 or not table.is_cuda \
+                or not table.is_contiguous() or tuple(table.shape) != shape:
+            raise SfError(SF_E_ARG, f"expected a contiguous float32 device tensor of shape {shape}")
+        sf_set_recency_bias(self.handle, table, stream)
 
     def rope_rows(self, t, src, dst=None, stream=None):
         """The rotation the session's rope mode applies at frame t (in place when dst is None)."""

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsf.so")
-SOURCES = ["sf_host.cpp", "sf_copy.hip", "sf_rope.hip", "sf_attn.hip", "sf_attn_sk.hip"]
+SOURCES = ["sf_host.cpp", "sf_copy.hip", "sf_rope.hip", "sf_bias.hip", "sf_attn.hip", "sf_attn_sk.hip"]
 # Per-file code generation flags.  The attention kernels: MFMA results stay in
 # VGPRs (no AGPR round trips), and IEEE mode is off so max chains become v_max3
 # (no NaN canonicalisation; the kernels compute nothing on NaN inputs).

@@ -34,6 +34,11 @@
 //   range of units and the head's K/V stays in that XCD's L2.
 //   With split > 1 each unit writes an unnormalised partial (O, reference
 //   max, row sum) and combine_kernel merges the splits.
+//   Recency bias (BIAS = true; the page's section "Files" lists an optional
+//   recency bias on summary keys): each tile also stages its 64 keys' biases
+//   (log2 units, one fp32 per buffer row and head) in LDS, and the scores
+//   become S*c + bias in one FMA before the softmax.  A session without a
+//   bias in such a launch reads zeros.
 //
 // fp32 kernel (attn_f32_kernel<D>): one thread per query row, K/V tiles of a
 //   few keys broadcast from LDS, exact online softmax in fp32 on VALU.
@@ -72,6 +77,8 @@ struct Unit {
   const char* v;
   float* part_o;
   float* part_ml;
+  const float* bias;  // recency bias per buffer row, [H][bias_stride] log2 units, or NULL
+  int bias_stride;
   int rows, n_keys, split, ks, qt, h;
   int seg_row[SF_MAX_SEGMENTS];  // first buffer row of segment i
   int seg_key[SF_MAX_SEGMENTS];  // first flattened key of segment i (INT_MAX when unused)
@@ -92,6 +99,8 @@ __device__ __forceinline__ Unit decode_unit(const AttnLaunch& a, int unit, bool 
   u.v = reinterpret_cast<const char*>(S.v);
   u.part_o = S.part_o;
   u.part_ml = S.part_ml;
+  u.bias = S.bias;
+  u.bias_stride = S.bias_stride;
   u.rows = S.rows;
   u.n_keys = S.n_keys;
   u.split = with_split ? S.split : 1;
@@ -147,7 +156,7 @@ struct Tile {
 // p stays <= 2^15 in the accumulators, and p of the first tile (reference -inf) is inf.
 constexpr float kSumLimit = 32768.0f;
 
-template <int D>
+template <int D, bool BIAS>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a) {
   using T = Tile<D>;
   constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
@@ -155,7 +164,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   constexpr int KSTEPS = D / 16;             // MFMA k-steps over head_dim
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
   static_assert(PER * kThreads == BN * CH, "tile loads divide evenly");
-  __shared__ __attribute__((aligned(16))) char sm[2 * T::STAGE];
+  static_assert(BN <= kThreads, "one thread stages each key's bias");
+  constexpr int BIAS_OFF = 2 * T::STAGE;    // two stages of BN fp32 biases follow the K/V stages
+  __shared__ __attribute__((aligned(16))) char sm[2 * T::STAGE + (BIAS ? 2 * BN * 4 : 0)];
 
   const int unit = unit_of_block(a.total_units);
   if (unit >= a.total_units) return;
@@ -177,6 +188,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   const float c = a.scale_log2;
   const int row_stride = H * D;       // elements per buffer row
   const int row_bytes = 2 * row_stride;
+  // recency bias of this head's rows (log2 units), NULL when the session has none
+  const float* __restrict__ brow = BIAS && U.bias ? U.bias + (size_t)U.h * U.bias_stride : nullptr;
 
   // Q^T operand: lane holds Q[qrow][16*kk + 8*g .. +7] for every k-step (rows past R read row R-1).
   bf16x8 qreg[KSTEPS];
@@ -216,9 +229,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   // run of rows: a scalar base plus the fixed per-thread offsets.  Otherwise each
   // row is looked up; keys past the unit's range re-read its last key (finite
   // data) and get score -inf.
-#define SF_LOAD_TILE(TILE, KR, VR)                                                          \
+#define SF_LOAD_TILE(TILE, KR, VR, BR)                                                      \
   {                                                                                         \
     const int kap0_ = (TILE) * BN;                                                          \
+    if constexpr (BIAS) {                                                                   \
+      if (tid < BN) BR = brow ? brow[key_row(U, min(kap0_ + tid, key_hi - 1))] : 0.0f;      \
+    }                                                                                       \
     int srow_ = U.seg_row[0], skey_ = U.seg_key[0], send_ = U.seg_key[1];                   \
     _Pragma("unroll") for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {                           \
       const bool in_ = kap0_ >= U.seg_key[i];                                               \
@@ -241,10 +257,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
       }                                                                                     \
     }                                                                                       \
   }
-#define SF_STORE_TILE(STAGE_BYTES, KR, VR)                                                  \
+#define SF_STORE_TILE(STAGE_BYTES, KR, VR, BR)                                              \
   _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                         \
     *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + ksoff + p * RSTEP * T::ROW) = KR[p];     \
     *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + vsoff + p * RSTEP * T::ROW) = VR[p];     \
+  }                                                                                         \
+  if constexpr (BIAS) {                                                                     \
+    if (tid < BN) reinterpret_cast<float*>(sm + BIAS_OFF + ((STAGE_BYTES) / T::STAGE) * BN * 4)[tid] = BR; \
   }
 
   f32x16 o[DBLK];
@@ -279,16 +298,35 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
         if (kb + 32 >= key_hi) s1[r] = -INFINITY;
       }
     }
+    // ---- recency bias: scores to log2 units with each key's bias added (register r of
+    // block b holds key 32b + 8(r/4) + 4g + r%4); from here on the scale is 1.
+    if constexpr (BIAS) {
+      const float* bs = reinterpret_cast<const float*>(sm + BIAS_OFF + (ST / T::STAGE) * BN * 4);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 b0 = *reinterpret_cast<const float4*>(bs + 8 * q4 + 4 * g);
+        const float4 b1 = *reinterpret_cast<const float4*>(bs + 32 + 8 * q4 + 4 * g);
+        s0[4 * q4 + 0] = __builtin_fmaf(s0[4 * q4 + 0], c, b0.x);
+        s0[4 * q4 + 1] = __builtin_fmaf(s0[4 * q4 + 1], c, b0.y);
+        s0[4 * q4 + 2] = __builtin_fmaf(s0[4 * q4 + 2], c, b0.z);
+        s0[4 * q4 + 3] = __builtin_fmaf(s0[4 * q4 + 3], c, b0.w);
+        s1[4 * q4 + 0] = __builtin_fmaf(s1[4 * q4 + 0], c, b1.x);
+        s1[4 * q4 + 1] = __builtin_fmaf(s1[4 * q4 + 1], c, b1.y);
+        s1[4 * q4 + 2] = __builtin_fmaf(s1[4 * q4 + 2], c, b1.z);
+        s1[4 * q4 + 3] = __builtin_fmaf(s1[4 * q4 + 3], c, b1.w);
+      }
+    }
+    const float cs = BIAS ? 1.0f : c;
     // ---- P = exp2(S*c - mref) in bf16 and its row sum, against the current reference.
     bf16x8 pb[4];
     float ts;
     auto probs = [&]() {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        pb[0][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -mref));
-        pb[1][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 + r], c, -mref));
-        pb[2][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -mref));
-        pb[3][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 + r], c, -mref));
+        pb[0][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cs, -mref));
+        pb[1][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 + r], cs, -mref));
+        pb[2][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cs, -mref));
+        pb[3][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 + r], cs, -mref));
       }
       float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -307,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
       float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = max3(mt, s0[r], s1[r]);
-      mt = fmaxf(mt, xor32(mt)) * c;
+      mt = fmaxf(mt, xor32(mt)) * cs;
       const float mnew = fmaxf(mref, mt);
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
 #pragma unroll
@@ -337,21 +375,22 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   // Pipeline: tile i is computed from stage i&1 while tile i+2 is in flight in one
   // register set and tile i+1 (the other set) is stored to stage (i+1)&1 after it.
   u32x4 kra[PER], vra[PER], krb[PER], vrb[PER];
-  SF_LOAD_TILE(t0, kra, vra)
-  if (t0 + 1 < t1) SF_LOAD_TILE(t0 + 1, krb, vrb)
-  SF_STORE_TILE(0, kra, vra)
+  float bra = 0.0f, brb = 0.0f;  // this thread's key bias of each set (BIAS only)
+  SF_LOAD_TILE(t0, kra, vra, bra)
+  if (t0 + 1 < t1) SF_LOAD_TILE(t0 + 1, krb, vrb, brb)
+  SF_STORE_TILE(0, kra, vra, bra)
   __syncthreads();
   for (int tile = t0; tile < t1; tile += 2) {
     // even step: compute stage 0, refill set a with tile+2, store set b (tile+1) to stage 1
-    if (tile + 2 < t1) SF_LOAD_TILE(tile + 2, kra, vra)
+    if (tile + 2 < t1) SF_LOAD_TILE(tile + 2, kra, vra, bra)
     if (wave_on) compute_tile(tile, 0);
-    if (tile + 1 < t1) SF_STORE_TILE(T::STAGE, krb, vrb)
+    if (tile + 1 < t1) SF_STORE_TILE(T::STAGE, krb, vrb, brb)
     __syncthreads();
     if (tile + 1 >= t1) break;
     // odd step: compute stage 1, refill set b with tile+3, store set a (tile+2) to stage 0
-    if (tile + 3 < t1) SF_LOAD_TILE(tile + 3, krb, vrb)
+    if (tile + 3 < t1) SF_LOAD_TILE(tile + 3, krb, vrb, brb)
     if (wave_on) compute_tile(tile + 1, T::STAGE);
-    if (tile + 2 < t1) SF_STORE_TILE(0, kra, vra)
+    if (tile + 2 < t1) SF_STORE_TILE(0, kra, vra, bra)
     __syncthreads();
   }
 #undef SF_LOAD_TILE
@@ -422,11 +461,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnLaunch a) {
 // ---------------------------------------------------------------- fp32 path
 constexpr int kF32Threads = kF32RowsPerTile;
 
-template <int D>
+template <int D, bool BIAS>
 __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch a) {
   constexpr int KT = D <= 64 ? 16 : 8;  // keys per LDS tile
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
+  __shared__ float bs[KT];  // recency bias of the tile's keys, log2 units (BIAS only)
   const int unit = (int)wg_x();
   if (unit >= a.total_units) return;
   const Unit U = decode_unit(a, unit, false);
@@ -439,6 +479,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
   const float* __restrict__ vg = reinterpret_cast<const float*>(U.v) + U.h * D;
   const float c = a.scale_log2;
   const int n_keys = U.n_keys;
+  const float* __restrict__ brow = BIAS && U.bias ? U.bias + (size_t)U.h * U.bias_stride : nullptr;
 
   float q[D], o[D];
   {
@@ -457,6 +498,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
       ks[j][d] = kg[off];
       vs[j][d] = vg[off];
     }
+    if constexpr (BIAS) {
+      if (tid < KT) bs[tid] = brow ? brow[key_row(U, min(base + tid, n_keys - 1))] : 0.0f;
+    }
     __syncthreads();
     float s[KT];
     float mt = -INFINITY;
@@ -465,7 +509,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnLaunch 
       float acc = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], ks[j][d], acc);
-      s[j] = (base + j < n_keys) ? acc * c : -INFINITY;
+      s[j] = (base + j < n_keys) ? (BIAS ? __builtin_fmaf(acc, c, bs[j]) : acc * c) : -INFINITY;
       mt = fmaxf(mt, s[j]);
     }
     const float mnew = fmaxf(m, mt);
@@ -498,12 +542,16 @@ size_t attend_scratch_bytes(int64_t rows, int n_heads, int head_dim) {
   return (size_t)kMaxSplit * (size_t)rows * (size_t)n_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream) {
+hipError_t launch_attend_bf16(const AttnLaunch& a, bool bias, hipStream_t stream) {
   const int grid = round_up8(a.total_units);
-  if (a.head_dim == 64)
-    launch(attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), stream, a);
+  if (a.head_dim == 64 && bias)
+    launch(attn_bf16_kernel<64, true>, dim3(grid), dim3(kThreads), stream, a);
+  else if (a.head_dim == 64)
+    launch(attn_bf16_kernel<64, false>, dim3(grid), dim3(kThreads), stream, a);
+  else if (a.head_dim == 128 && bias)
+    launch(attn_bf16_kernel<128, true>, dim3(grid), dim3(kThreads), stream, a);
   else if (a.head_dim == 128)
-    launch(attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), stream, a);
+    launch(attn_bf16_kernel<128, false>, dim3(grid), dim3(kThreads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -527,11 +575,15 @@ hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream) {
-  if (a.head_dim == 64)
-    launch(attn_f32_kernel<64>, dim3(a.total_units), dim3(kF32Threads), stream, a);
+hipError_t launch_attend_f32(const AttnLaunch& a, bool bias, hipStream_t stream) {
+  if (a.head_dim == 64 && bias)
+    launch(attn_f32_kernel<64, true>, dim3(a.total_units), dim3(kF32Threads), stream, a);
+  else if (a.head_dim == 64)
+    launch(attn_f32_kernel<64, false>, dim3(a.total_units), dim3(kF32Threads), stream, a);
+  else if (a.head_dim == 128 && bias)
+    launch(attn_f32_kernel<128, true>, dim3(a.total_units), dim3(kF32Threads), stream, a);
   else if (a.head_dim == 128)
-    launch(attn_f32_kernel<128>, dim3(a.total_units), dim3(kF32Threads), stream, a);
+    launch(attn_f32_kernel<128, false>, dim3(a.total_units), dim3(kF32Threads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -46,7 +46,8 @@ constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 31;
 int64_t elem_bytes(int32_t dtype) { return dtype == SF_BF16 ? 2 : 4; }
 
 struct Geo {
-  int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, qrot_off, total;
+  int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, qrot_off;
+  int64_t bias_tab_off, bias_tab_bytes, bias_row_off, total;
 };
 
 // Dims of the temporal band of a head (Wan2.1 split: hd - 4*floor(hd/6), first in the head).
@@ -68,7 +69,7 @@ sf_status check_config(const sf_config* c, std::string* why) {
     return SF_E_ARG;
   }
   if (c->dtype != SF_F32 && c->dtype != SF_BF16) { *why = "dtype must be SF_F32 or SF_BF16"; return SF_E_ARG; }
-  if (c->reserved != 0) { *why = "reserved must be 0"; return SF_E_ARG; }
+  if (c->recency_bias != 0 && c->recency_bias != 1) { *why = "recency_bias must be 0 or 1"; return SF_E_ARG; }
   if (c->rope_mode != SF_ROPE_CALLER && c->rope_mode != SF_ROPE_LEVEL_REPLACE && c->rope_mode != SF_ROPE_LEVEL_ADD) {
     *why = "rope_mode must be SF_ROPE_CALLER, SF_ROPE_LEVEL_REPLACE or SF_ROPE_LEVEL_ADD";
     return SF_E_ARG;
@@ -107,13 +108,23 @@ Geo geometry(const sf_config* c) {
   g.block_stride = 2 * g.tensor_bytes;
   g.kv_bytes = g.block_stride * c->n_blocks;
   g.scratch_off = (g.kv_bytes + 255) / 256 * 256;
+  // bf16 head_dim 64 reads through the stream-K kernel, or the split-key kernel with a recency bias
   g.scratch_bytes = c->dtype != SF_BF16 ? 0
-                    : c->head_dim == 64 ? (int64_t)sf::sk_scratch_bytes(g.R, c->n_heads, g.C)
-                                        : (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim);
+                    : c->head_dim == 64 && !c->recency_bias
+                        ? (int64_t)sf::sk_scratch_bytes(g.R, c->n_heads, g.C)
+                        : (int64_t)sf::attend_scratch_bytes(g.R, c->n_heads, c->head_dim);
+  auto align256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+  int64_t end = g.scratch_off + g.scratch_bytes;
   // a rotated query (rope modes): R rows, 256-byte aligned after the scratch
-  g.qrot_off = (g.scratch_off + g.scratch_bytes + 255) / 256 * 256;
-  g.total = c->rope_mode == SF_ROPE_CALLER ? g.scratch_off + g.scratch_bytes
-                                           : g.qrot_off + g.R * g.row_elems * elem_bytes(c->dtype);
+  g.qrot_off = align256(end);
+  if (c->rope_mode != SF_ROPE_CALLER) end = g.qrot_off + g.R * g.row_elems * elem_bytes(c->dtype);
+  // recency bias: the table [H][W+1] (zero-filled at create, padded to 256 bytes), then
+  // the per-row biases of the current frame [H][C], fp32
+  g.bias_tab_off = align256(end);
+  g.bias_tab_bytes = c->recency_bias ? align256((int64_t)c->n_heads * (c->w + 1) * 4) : 0;
+  g.bias_row_off = g.bias_tab_off + g.bias_tab_bytes;
+  if (c->recency_bias) end = g.bias_row_off + (int64_t)c->n_heads * g.C * 4;
+  g.total = end;
   return g;
 }
 
@@ -232,6 +243,7 @@ struct sf_buffer {
   bool fail_next = false;
   std::string err;
   Tracer trace;
+  int64_t bias_t = -1;  // frame whose per-row recency biases the device holds; -1: none
 };
 
 namespace {
@@ -463,6 +475,29 @@ sf_status stage_query(sf_buffer* b, const void* q, const void** qs, hipStream_t 
   return SF_OK;
 }
 
+// [files], [credits] The per-row recency biases for the session's current frame, rebuilt on
+// the read's stream when the frame (or the table) changed since the last build.
+sf_status refresh_bias(sf_buffer* b, hipStream_t st) {
+  const sf_config& c = b->cfg;
+  if (!c.recency_bias || b->dry || b->bias_t == b->slots.t_cur) return SF_OK;
+  sf::BiasGeo g;
+  g.rows = (int32_t)b->geo.R;
+  g.hw = c.hw;
+  g.x = c.x;
+  g.y = c.y;
+  g.w = c.w;
+  g.heads = c.n_heads;
+  g.capacity = (int32_t)b->geo.C;
+  g.pad = 0;
+  g.t = b->slots.t_cur;
+  TraceScope ts(b->trace, SF_K_BIAS, st);
+  hipError_t e = sf::launch_bias_rows(reinterpret_cast<float*>(b->mem + b->geo.bias_row_off),
+                                      reinterpret_cast<const float*>(b->mem + b->geo.bias_tab_off), g, st);
+  if (e != hipSuccess) return hip_fail(b, e, "recency bias launch");
+  b->bias_t = b->slots.t_cur;
+  return SF_OK;
+}
+
 // Compute units of the current device (cached per device).
 int device_cu_count() {
   static int cache[64] = {0};
@@ -598,13 +633,11 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
   return SF_OK;
 }
 
-sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
-                         float scale, hipStream_t st) {
+// The split-key (bf16) or fp32 read; sessions with a recency bias get their per-row biases.
+sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
+                               void* const* out, float scale_log2, hipStream_t st) {
   sf_buffer* b0 = bufs[0];
   const sf_config& c0 = b0->cfg;
-  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c0.head_dim);
-  const float scale_log2 = sc * 1.4426950408889634f;
-  if (c0.dtype == SF_BF16 && c0.head_dim == 64) return enqueue_attend_sk(bufs, n, block, q, out, scale_log2, st);
   for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
     const int cnt = n - first < sf::kMaxLaunchSessions ? n - first : sf::kMaxLaunchSessions;
     sf::AttnLaunch a;
@@ -633,9 +666,17 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     const char* split_env = std::getenv("SF_ATTN_SPLIT");
     const int forced_split = split_env ? std::atoi(split_env) : 0;
     int64_t units = 0;
+    bool any_bias = false;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       sf::AttnSession& s = a.s[i];
+      if (b->cfg.recency_bias) {
+        sf_status r = refresh_bias(b, st);
+        if (r != SF_OK) return fail(b0, r, b->err);
+        s.bias = reinterpret_cast<const float*>(b->mem + b->geo.bias_row_off);
+        s.bias_stride = (int32_t)b->geo.C;
+        any_bias = true;
+      }
       s.q = q[first + i];
       s.out = static_cast<float*>(out[first + i]);
       s.k = b->mem + block * b->geo.block_stride;
@@ -668,7 +709,7 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     hipError_t e;
     {
       TraceScope ts(b0->trace, SF_K_ATTEND, st);
-      e = bf16 ? sf::launch_attend_bf16(a, st) : sf::launch_attend_f32(a, st);
+      e = bf16 ? sf::launch_attend_bf16(a, any_bias, st) : sf::launch_attend_f32(a, any_bias, st);
     }
     if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
     if (bf16) {
@@ -678,6 +719,32 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     }
   }
   return SF_OK;
+}
+
+sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
+                         float scale, hipStream_t st) {
+  const sf_config& c0 = bufs[0]->cfg;
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c0.head_dim);
+  const float scale_log2 = sc * 1.4426950408889634f;
+  if (c0.dtype != SF_BF16 || c0.head_dim != 64) return enqueue_attend_split(bufs, n, block, q, out, scale_log2, st);
+  // bf16 head_dim 64: the stream-K kernel, except for sessions with a recency bias
+  sf_buffer* gb[2][SF_MAX_BATCH];
+  const void* gq[2][SF_MAX_BATCH];
+  void* go[2][SF_MAX_BATCH];
+  int cnt[2] = {0, 0};
+  for (int i = 0; i < n; ++i) {
+    const int k = bufs[i]->cfg.recency_bias ? 1 : 0;
+    gb[k][cnt[k]] = bufs[i];
+    gq[k][cnt[k]] = q[i];
+    go[k][cnt[k]] = out[i];
+    ++cnt[k];
+  }
+  if (cnt[0] > 0) {
+    sf_status s = enqueue_attend_sk(gb[0], cnt[0], block, gq[0], go[0], scale_log2, st);
+    if (s != SF_OK) return s;
+  }
+  if (cnt[1] == 0) return SF_OK;
+  return enqueue_attend_split(gb[1], cnt[1], block, gq[1], go[1], scale_log2, st);
 }
 
 void fill_view(const sf_config& c, const Geo& g, const Slots& s, int32_t blocks_written, sf_view* v) {
@@ -756,6 +823,9 @@ sf_status sf_buffer_create(const sf_config* cfg, void* dev_mem, size_t bytes, vo
   b->written_at.assign(cfg->n_blocks, -1);
   if (!dry) {
     hipError_t e = sf::launch_fill_zero(dev_mem, (size_t)g.kv_bytes, static_cast<hipStream_t>(hip_stream));
+    if (e == hipSuccess && g.bias_tab_bytes > 0)
+      e = sf::launch_fill_zero(static_cast<char*>(dev_mem) + g.bias_tab_off, (size_t)g.bias_tab_bytes,
+                               static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) {
       delete b;
       return fail(nullptr, SF_E_HIP, std::string("zero fill launch: ") + hipGetErrorString(e));
@@ -876,6 +946,7 @@ sf_status sf_state_import(sf_buffer* buf, const void* src, size_t bytes) {
   if (!ok) return fail(buf, SF_E_ARG, "sf_state_import: inconsistent state");
   buf->slots = s;
   buf->written_at = wa;
+  buf->bias_t = -1;
   return SF_OK;
 }
 
@@ -947,6 +1018,7 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   auto restore = [&](sf_status r) {
     buf->slots = saved;
     buf->written_at = saved_written;
+    buf->bias_t = -1;  // the device may hold the biases of the frame this call advanced to
     return r;
   };
   if (evict_due) {
@@ -958,9 +1030,11 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   void* outs[1] = {out};
   // bf16, head_dim 64: the attention launch writes the record itself (and reads its keys
   // from k and v) whenever the block has a full 64-key tile after the write and the rows
-  // around the record fit the remaining segment slots.  Not under a rope mode: there the
-  // stored keys are the turned ones, written first.
-  if (!buf->dry && buf->cfg.dtype == SF_BF16 && buf->cfg.head_dim == 64 && buf->cfg.rope_mode == SF_ROPE_CALLER) {
+  // around the record fit the remaining segment slots.  Not under a rope mode (there the
+  // stored keys are the turned ones, written first), nor with a recency bias (that read
+  // goes through the split-key kernel).
+  if (!buf->dry && buf->cfg.dtype == SF_BF16 && buf->cfg.head_dim == 64 && buf->cfg.rope_mode == SF_ROPE_CALLER &&
+      !buf->cfg.recency_bias) {
     write_state(buf, block, t);
     Segs sg;
     readable(buf->cfg, buf->geo, buf->slots, &sg);
@@ -992,6 +1066,23 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   if (buf->dry) return SF_OK;
   s = enqueue_attend(one, 1, block, qs, outs, scale, st);
   if (s != SF_OK) return restore(s);
+  return SF_OK;
+}
+
+sf_status sf_set_recency_bias(sf_buffer* buf, const float* table, void* hip_stream) {
+  if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
+  const sf_config& c = buf->cfg;
+  if (!c.recency_bias) return fail(buf, SF_E_UNSUPPORTED, "sf_set_recency_bias: the config has recency_bias = 0");
+  if (!buf->dry && (!table || (reinterpret_cast<uintptr_t>(table) & 3u)))
+    return fail(buf, SF_E_ARG, "sf_set_recency_bias: table is NULL or not 4-byte aligned");
+  if (take_injected(buf)) return fail(buf, SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
+  if (buf->dry) return SF_OK;
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  TraceScope ts(buf->trace, SF_K_BIAS, st);
+  hipError_t e = sf::launch_bias_table(reinterpret_cast<float*>(buf->mem + buf->geo.bias_tab_off), table,
+                                       c.n_heads * (c.w + 1), st);
+  if (e != hipSuccess) return hip_fail(buf, e, "recency bias table launch");
+  buf->bias_t = -1;
   return SF_OK;
 }
 

@@ -1,5 +1,5 @@
 // Private interface between the host state machine (sf_host.cpp) and the
-// gfx950 kernels (sf_copy.hip, sf_rope.hip, sf_attn.hip, sf_attn_sk.hip).
+// gfx950 kernels (sf_copy.hip, sf_rope.hip, sf_bias.hip, sf_attn.hip, sf_attn_sk.hip).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -51,6 +51,9 @@ struct AttnSession {
   const void* v;        // this block's V [C][H][D]
   float* part_o;        // [split][rows][H][D] fp32 partial numerators (split > 1)
   float* part_ml;       // [split][rows][H][2] fp32 (reference max in log2 units, row sum)
+  const float* bias;    // recency bias per buffer row, log2 units, [H][bias_stride]; NULL: none
+  int32_t bias_stride;  // rows per head in `bias` (the capacity C)
+  int32_t pad_;
   int32_t rows;         // query rows (R)
   int32_t n_keys;       // readable rows
   int32_t n_seg;        // readable row segments (<= SF_MAX_SEGMENTS)
@@ -170,8 +173,26 @@ struct RopeJob {
 };
 hipError_t launch_rope_rows(const RopeJob& job, int rows, int hw, int heads, int head_dim, bool bf16,
                             int level_mode, const SinkTable& tab, hipStream_t stream);
-hipError_t launch_attend_bf16(const AttnLaunch& a, hipStream_t stream);
-hipError_t launch_attend_f32(const AttnLaunch& a, hipStream_t stream);
+// Recency bias: copies a caller's table [heads][w+1] (n floats) into the session memory.
+hipError_t launch_bias_table(float* dst, const float* src, int n, hipStream_t stream);
+// Recency bias per buffer row at frame t: dst[h][row] = log2(e) * tab[h][age] for a
+// summary row of a generated frame (age = t - its frame, from the slot formulas), 0 for raw
+// rows and for Z0; values below -1e30 are raised to it.
+struct BiasGeo {
+  int32_t rows;      // R
+  int32_t hw;
+  int32_t x;
+  int32_t y;
+  int32_t w;
+  int32_t heads;
+  int32_t capacity;  // C
+  int32_t pad;
+  int64_t t;
+};
+hipError_t launch_bias_rows(float* dst, const float* tab, const BiasGeo& g, hipStream_t stream);
+// bias: any session has a recency bias (kernels that read AttnSession::bias).
+hipError_t launch_attend_bf16(const AttnLaunch& a, bool bias, hipStream_t stream);
+hipError_t launch_attend_f32(const AttnLaunch& a, bool bias, hipStream_t stream);
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream);
 
 }  // namespace sf

@@ -25,6 +25,10 @@
  *              a head's temporal RoPE planes turn by under half a radian over 1024
  *              frames; summary tokens take an exact quarter turn on them, and the
  *              model refuses to build unless they are idle.
+ *   [files]    "Files": the model's files include an optional recency bias on
+ *              summary keys.
+ *   [credits]  "Credits": that bias follows the Recency Forcing paper, which the
+ *              page does not reproduce.
  *
  * Terms.  A session is one player's memory: n_blocks independent buffers,
  * one per transformer block, stepped together frame by frame.  R = hw + x
@@ -41,7 +45,8 @@
  * b * 2 * C*n_heads*head_dim*elem, V_b follows K_b); after the last block
  * comes a scratch region that sf_attend uses for partial results of this
  * session (and, when the library applies the temporal band, room for one rotated
- * query).  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
+ * query; with the recency bias on, its table and the per-row biases of the
+ * current frame).  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
  *
  * Tensors passed per call (device pointers, row-major, contiguous):
  *   q, k, v : [R][n_heads][head_dim] in the config dtype (fp32 or bf16)
@@ -119,7 +124,9 @@ typedef struct sf_config {
                          the page's table follows Wan2.1: 10000); read only when sink_gap > 0
                          or rope_mode != SF_ROPE_CALLER */
   int32_t rope_mode;  /* [level] sf_rope_mode */
-  int32_t reserved;   /* must be 0 */
+  int32_t recency_bias; /* [files], [credits] 0 = off, 1 = on: the read adds a per-head term,
+                         set by sf_set_recency_bias, to the scaled scores of summary keys by the
+                         age of their frame (starts at 0) */
 } sf_config;
 
 #define SF_MAX_SEGMENTS 4
@@ -157,8 +164,9 @@ int64_t sf_kv_offset(const sf_config* cfg, int32_t block, int32_t which);
 
 /* [buffer] One preallocated buffer per block.  Binds dev_mem (>= sf_buffer_bytes, 16-byte
  * aligned, owned by the caller, valid until destroy and until enqueued work ends) to a new
- * handle and enqueues a zero fill of the K/V bytes on stream, so empty slots read as zero.
- * dev_mem == NULL with bytes == 0 makes a dry-run handle. */
+ * handle and enqueues a zero fill of the K/V bytes (and of the recency bias table, when the
+ * config has one) on stream, so empty slots read as zero.  dev_mem == NULL with bytes == 0
+ * makes a dry-run handle. */
 sf_status sf_buffer_create(const sf_config* cfg, void* dev_mem, size_t bytes, void* hip_stream,
                            sf_buffer** out);
 
@@ -222,9 +230,28 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
  * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One launch
  * (plus a combine launch when the key range is split) for the whole batch.
  * [level] A session under SF_ROPE_LEVEL_* takes q unrotated: it is turned by that session's
- * t_cur (as sf_rope_rows does) into the session's own memory first, one launch per session. */
+ * t_cur (as sf_rope_rows does) into the session's own memory first, one launch per session.
+ * [files], [credits] A session with recency_bias = 1 adds its bias (sf_set_recency_bias) to
+ * the scores of summary keys; a batch is launched per read path (sessions with and without
+ * the bias at bf16 head_dim 64 take different kernels). */
 sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
                     void* const* out, float scale, void* hip_stream);
+
+/* [files], [credits] The recency bias of a session configured with recency_bias = 1.
+ * table: device pointer to [n_heads][w+1] fp32 (4-byte aligned, read by this call's launch
+ * only; NULL allowed on a dry-run handle).  Entry [h][a] is added, in natural-log units, to
+ * head h's scaled scores scale * <q, k> against every summary row (record rows [hw, R)) of
+ * the generated frame a frames older than the current frame t_cur, wherever that row is:
+ * the record of t_cur itself (a = 0), a RAW slot (a = 1..y) or a SUM slot (a = y+1..w).  Raw
+ * rows and Z0's rows (the start image) get no bias.  Entries must not be NaN; -inf (or any
+ * value below -1e30) drops those keys.  The table is copied into the session memory on the
+ * stream (one launch) and holds for every later read until set again; before the first call
+ * it is all zeros.  The per-row biases of the current frame are rebuilt on the read's
+ * stream by the first read of each frame (one small launch).  Reads of such a session go
+ * through the split-key attention kernel at every head_dim, and sf_step writes the record
+ * before the read (no fused write).  SF_E_UNSUPPORTED when the config has recency_bias = 0;
+ * SF_E_ARG for a NULL or misaligned table. */
+sf_status sf_set_recency_bias(sf_buffer* buf, const float* table, void* hip_stream);
 
 /* One block of one frame: sf_evict(t) if it is due and has not run, then sf_write_record,
  * then sf_attend of this session alone (q and k unrotated under SF_ROPE_LEVEL_*). */
@@ -260,9 +287,10 @@ sf_status sf_debug_fail_next_launch(sf_buffer* buf);
  * alone.  sf_kernel_times_read waits for those events, returns the summed milliseconds and
  * launch counts per kind since the last read, and starts a new period.  Kinds (ATTEND: the main attention kernel; TAIL: keys past the
  * last full 64-key tile of a bf16 head_dim-64 read; COMBINE: merging of split results; SINK:
- * the rotation of Z0's keys; ROPE: the rotation of a query before a read): */
+ * the rotation of Z0's keys; ROPE: the rotation of a query before a read; BIAS: the copy of a
+ * recency bias table and the rebuild of the per-row biases): */
 enum { SF_K_FILL = 0, SF_K_WRITE = 1, SF_K_EVICT = 2, SF_K_ATTEND = 3, SF_K_COMBINE = 4, SF_K_TAIL = 5,
-       SF_K_SINK = 6, SF_K_ROPE = 7, SF_K_KINDS = 8 };
+       SF_K_SINK = 6, SF_K_ROPE = 7, SF_K_BIAS = 8, SF_K_KINDS = 9 };
 typedef struct sf_kernel_times {
   double ms[SF_K_KINDS];
   int64_t launches[SF_K_KINDS];

@@ -21,6 +21,7 @@ from __future__ import annotations
 import torch
 
 Q, K, V = 0, 1, 2
+BIAS = 3  # a recency bias table (one per session)
 
 # name -> shape and seed of each workload.  Keys mirror the C-ABI's sf_config
 # fields; "frames" lists the frame ids a workload steps through (or, for the
@@ -55,7 +56,7 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 def tensor_key(seed: int, session: int, block: int, t: int, which: int) -> int:
     """64-bit generator seed naming one tensor (seed, session, block, frame, Q/K/V)."""
-    if not (0 <= session < 256 and 0 <= block < 256 and 0 <= t < (1 << 20) and which in (Q, K, V)):
+    if not (0 <= session < 256 and 0 <= block < 256 and 0 <= t < (1 << 20) and which in (Q, K, V, BIAS)):
         raise ValueError("tensor_key: field out of range")
     return ((((seed * 256 + session) * 256 + block) << 20 | t) << 4) | which
 
@@ -83,6 +84,12 @@ def frame_tensors(wl: dict, session: int, block: int, t: int, device="cpu"):
     k = draw(shp, tensor_key(seed, session, block, t, K), dt, device)
     v = draw(shp, tensor_key(seed, session, block, t, V), dt, device, wl.get("v_scale", 1.0))
     return q, k, v
+
+
+def bias_table(wl: dict, session: int, version: int = 0, scale: float = 2.0, device="cpu") -> torch.Tensor:
+    """A recency bias table [n_heads][w + 1] in float32: i.i.d. N(0, 1) times ``scale``,
+    drawn from the generator of (seed, session, block 0, frame ``version``, BIAS)."""
+    return draw((wl["n_heads"], wl["w"] + 1), tensor_key(wl["seed"], session, 0, version, BIAS), "f32", device, scale)
 
 
 def to_host_bytes(x: torch.Tensor):

@@ -398,6 +398,36 @@ def test_rope_mode_sizes_and_rules():
             sf.sf_rope_rows(cfg, t, src, 16)
         assert ei.value.status == code
     bad = sf.make_config(**GEOMS["tiny"])
-    bad.reserved = 1
+    bad.recency_bias = 2
     with pytest.raises(sf.SfError):
         sf.sf_config_check(bad)
+
+
+def test_recency_bias_sizes_and_rules():
+    """[files], [credits] The recency bias: room for its table [H][W+1] and the per-row
+    biases [H][C] (fp32), the split-key scratch at bf16 head_dim 64, and its call rules."""
+    for name in ("tiny", "served"):
+        wl = GEOMS[name]
+        plain = sf.make_config(**wl)
+        cfg = sf.make_config(**dict(wl, recency_bias=True))
+        sf.sf_config_check(cfg)
+        h, w = wl["n_heads"], wl["w"]
+        r = wl["hw"] + wl["x"]
+        c = r * (wl["y"] + 2) + (w - wl["y"]) * wl["x"]
+        assert sf.sf_buffer_bytes(cfg) >= sf.sf_kv_bytes(cfg) + h * (w + 1) * 4 + h * c * 4
+        assert sf.sf_kv_bytes(cfg) == sf.sf_kv_bytes(plain)
+        if wl["dtype"] == "f32":                     # no scratch: exactly the bias regions more
+            assert sf.sf_buffer_bytes(cfg) - sf.sf_buffer_bytes(plain) >= h * (w + 1) * 4 + h * c * 4
+        s = sf.Session(cfg, dry=True)
+        s.set_recency_bias(None)                     # a dry handle takes no table
+        for t in range(12):                          # the bias changes no slot rule
+            advance(s, wl, t)
+            s.set_recency_bias(None)
+            p = sf.sf_plan(cfg, t)
+            assert all(s.view()[k] == p[k] for k in ("t_cur", "n_keys", "segments", "raw_frame", "sum_frame"))
+        with pytest.raises(sf.SfError) as ei:       # no bias in this config
+            sf.Session(plain, dry=True).set_recency_bias(None)
+        assert ei.value.status == sf.SF_E_UNSUPPORTED
+    with pytest.raises(sf.SfError) as ei:
+        sf.sf_set_recency_bias(0, None)
+    assert ei.value.status == sf.SF_E_ARG
