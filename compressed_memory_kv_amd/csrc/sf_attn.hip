@@ -428,7 +428,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
   }
 }
 
-// Merge key splits: one wave per (row, head); lane covers D/64 output columns.
+// Merge key splits: one wave per (row, head); lane covers D/64 output columns.  Every
+// split's partial (reference max, row sum, numerators) is loaded before the first use, so
+// a wave has all its loads in flight at once.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnLaunch a) {
   const AttnSession& S = a.s[wg_y()];
@@ -438,22 +440,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnLaunch a) {
   if (idx >= S.rows * H) return;
   const int lane = tid_x() & 63;
   const size_t slice = (size_t)S.rows * H;  // (row, head) pairs per split
-  float mmax = -INFINITY;
-  for (int k = 0; k < S.split; ++k) mmax = fmaxf(mmax, S.part_ml[(k * slice + idx) * 2]);
+  const int split = S.split;                // <= kMaxSplit
   constexpr int PER = D / 64;
+  float m[kMaxSplit], l[kMaxSplit], po[kMaxSplit][PER];
+#pragma unroll
+  for (int k = 0; k < kMaxSplit; ++k) {
+    m[k] = -INFINITY;
+    l[k] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) po[k][j] = 0.0f;
+    if (k < split) {
+      const float2 ml = *reinterpret_cast<const float2*>(S.part_ml + (k * slice + idx) * 2);
+      m[k] = ml.x;
+      l[k] = ml.y;
+      const float* p = S.part_o + (k * slice + idx) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) po[k][j] = p[lane + 64 * j];
+    }
+  }
+  float mmax = m[0];
+#pragma unroll
+  for (int k = 1; k < kMaxSplit; ++k) mmax = fmaxf(mmax, m[k]);
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
-  float l = 0.0f;
-  for (int k = 0; k < S.split; ++k) {
-    const float2 ml = *reinterpret_cast<const float2*>(S.part_ml + (k * slice + idx) * 2);
-    const float wgt = __builtin_amdgcn_exp2f(ml.x - mmax);
-    l += wgt * ml.y;
-    const float* po = S.part_o + (k * slice + idx) * D;
+  float lt = 0.0f;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[lane + 64 * j];
+  for (int k = 0; k < kMaxSplit; ++k) {
+    const float wgt = __builtin_amdgcn_exp2f(m[k] - mmax);  // 0 for the splits past `split`
+    lt += wgt * l[k];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[k][j];
   }
-  const float inv = 1.0f / l;
+  const float inv = 1.0f / lt;
 #pragma unroll
   for (int j = 0; j < PER; ++j) S.out[(size_t)idx * D + lane + 64 * j] = acc[j] * inv;
 }
