@@ -576,6 +576,24 @@ hipError_t launch_attend_bf16(const AttnLaunch& a, bool bias, hipStream_t stream
   return hipGetLastError();
 }
 
+int attend_bf16_wgs_per_cu(int head_dim, bool bias) {
+  // per device and variant; 0 until asked
+  static int cache[64][4] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  const int v = (head_dim == 128 ? 2 : 0) + (bias ? 1 : 0);
+  if (cache[dev][v] == 0) {
+    int n = 0;
+    hipError_t e;
+    if (v == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, false>, kThreads, 0);
+    else if (v == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, true>, kThreads, 0);
+    else if (v == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, false>, kThreads, 0);
+    else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, true>, kThreads, 0);
+    cache[dev][v] = (e == hipSuccess && n > 0) ? n : 1;
+  }
+  return cache[dev][v];
+}
+
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
   int max_pairs = 0;
   bool any = false;

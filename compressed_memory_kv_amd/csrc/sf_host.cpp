@@ -648,19 +648,39 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
     a.scale_log2 = scale_log2;
     const bool bf16 = c0.dtype == SF_BF16;
     const int rows_per_tile = bf16 ? sf::kBf16RowsPerTile : sf::kF32RowsPerTile;
-    // Key split: aim at about four workgroups per compute unit for the launch.
-    int64_t base_units = 0, total_tiles = 0;
+    // Key split.  When the (session, head, query tile) units fit in one round of resident
+    // workgroups, the split s minimises rounds(s) * ceil(tiles / s) + s (the last term for the
+    // combine's reads); otherwise aim at about four workgroups per compute unit.
+    int64_t base_units = 0, total_tiles = 0, max_tiles = 0;
+    bool launch_bias = false;
     std::vector<Segs> segs(cnt);
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       readable(b->cfg, b->geo, b->slots, &segs[i]);
       const int64_t qt = (b->geo.R + rows_per_tile - 1) / rows_per_tile;
+      const int64_t tiles = (segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile;
       base_units += qt * c0.n_heads;
-      total_tiles += qt * c0.n_heads * ((segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile);
+      total_tiles += qt * c0.n_heads * tiles;
+      max_tiles = tiles > max_tiles ? tiles : max_tiles;
+      launch_bias = launch_bias || b->cfg.recency_bias;
     }
     const int64_t target_units = 1024;
     int64_t tiles_per_unit = (total_tiles + target_units - 1) / target_units;
     if (tiles_per_unit < 4) tiles_per_unit = 4;
+    int64_t round_split = 0;
+    if (bf16 && base_units > 0) {
+      const int64_t slots = (int64_t)device_cu_count() * sf::attend_bf16_wgs_per_cu(c0.head_dim, launch_bias);
+      if (base_units <= slots) {
+        int64_t best = -1;
+        for (int64_t sp = 1; sp <= sf::kMaxSplit && sp <= (max_tiles > 0 ? max_tiles : 1); ++sp) {
+          const int64_t cost = (base_units * sp + slots - 1) / slots * ((max_tiles + sp - 1) / sp) + sp;
+          if (best < 0 || cost < best) {
+            best = cost;
+            round_split = sp;
+          }
+        }
+      }
+    }
     // SF_ATTN_SPLIT=n forces n key splits per (session, head, query tile) (tuning only:
     // results change only by rounding).
     const char* split_env = std::getenv("SF_ATTN_SPLIT");
@@ -694,7 +714,9 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
       int64_t split = 1;
       if (bf16) {
         const int64_t tiles = (segs[i].keys + sf::kBf16KeysPerTile - 1) / sf::kBf16KeysPerTile;
-        split = forced_split > 0 ? forced_split : (tiles + tiles_per_unit - 1) / tiles_per_unit;
+        split = forced_split > 0 ? forced_split
+                : round_split > 0 ? round_split
+                                  : (tiles + tiles_per_unit - 1) / tiles_per_unit;
         if (split > sf::kMaxSplit) split = sf::kMaxSplit;
         if (split > tiles) split = tiles;
         if (split < 1) split = 1;

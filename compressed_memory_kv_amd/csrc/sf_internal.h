@@ -190,6 +190,8 @@ struct BiasGeo {
   int64_t t;
 };
 hipError_t launch_bias_rows(float* dst, const float* tab, const BiasGeo& g, hipStream_t stream);
+// Workgroups of the bf16 split-key kernel that fit on one compute unit at once.
+int attend_bf16_wgs_per_cu(int head_dim, bool bias);
 // bias: any session has a recency bias (kernels that read AttnSession::bias).
 hipError_t launch_attend_bf16(const AttnLaunch& a, bool bias, hipStream_t stream);
 hipError_t launch_attend_f32(const AttnLaunch& a, bool bias, hipStream_t stream);
