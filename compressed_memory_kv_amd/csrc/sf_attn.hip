@@ -44,6 +44,7 @@
 //   few keys broadcast from LDS, exact online softmax in fp32 on VALU.
 #include "sf_internal.h"
 
+#include <atomic>
 #include <cmath>
 
 namespace sf {
@@ -577,21 +578,23 @@ hipError_t launch_attend_bf16(const AttnLaunch& a, bool bias, hipStream_t stream
 }
 
 int attend_bf16_wgs_per_cu(int head_dim, bool bias) {
-  // per device and variant; 0 until asked
-  static int cache[64][4] = {};
+  // per device and variant; 0 until asked (every thread that asks stores the same value)
+  static std::atomic<int> cache[64][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   const int v = (head_dim == 128 ? 2 : 0) + (bias ? 1 : 0);
-  if (cache[dev][v] == 0) {
+  int cached = cache[dev][v].load(std::memory_order_relaxed);
+  if (cached == 0) {
     int n = 0;
     hipError_t e;
     if (v == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, false>, kThreads, 0);
     else if (v == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, true>, kThreads, 0);
     else if (v == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, false>, kThreads, 0);
     else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, true>, kThreads, 0);
-    cache[dev][v] = (e == hipSuccess && n > 0) ? n : 1;
+    cached = (e == hipSuccess && n > 0) ? n : 1;
+    cache[dev][v].store(cached, std::memory_order_relaxed);
   }
-  return cache[dev][v];
+  return cached;
 }
 
 hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {

@@ -16,6 +16,7 @@
 //   "The rest of the model"     the clean pass rewrites the frame's entry.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -500,15 +501,15 @@ sf_status refresh_bias(sf_buffer* b, hipStream_t st) {
 
 // Compute units of the current device (cached per device).
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // 0 until asked; every thread that asks stores the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // bf16, head_dim 64: persistent stream-K kernel, then the combine of split units.
