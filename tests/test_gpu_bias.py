@@ -228,3 +228,33 @@ def test_bias_calls_and_launch_counts():
     assert times["bias"][1] == 1 + 5, times["bias"]
     assert times["attend"][1] == 10
     sf.sf_profile_enable(sess.handle, False)
+
+
+@needs_gpu
+@pytest.mark.timeout(900)
+def test_bias_long_horizon_sampled():
+    """The long-horizon shape (24 heads of 128, 46,688 keys, SUM ages up to W = 96), one
+    block, with a bias: slot tables every frame, the whole buffer at three frames, attention
+    on sampled query rows as the window fills and once it is full."""
+    wl = dict(sf_inputs.WORKLOADS["long"], n_blocks=1, recency_bias=True)
+    g = so.Geometry.from_workload(wl)
+    sess = sf.Session(sf.make_config(**wl))
+    orc = so.MemoryReplay(g)
+    tab = table(wl, 0, 0)
+    sess.set_recency_bias(tab)
+    orc.set_recency_bias(tab.cpu().numpy())
+    out = out_like(wl)
+    rows = np.unique(np.concatenate([np.arange(0, g.r, 256), np.arange(g.hw, g.r, 16), [g.r - 1]]))
+    for t in range(101):
+        q, k, v = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
+        sess.step(0, t, q, k, v, out)
+        orc.step(t, {0: (host(k), host(v))})
+        torch.cuda.synchronize()
+        check_tables(sess, orc, f"long t={t}")
+        if t in (6, 97, 100):
+            check_buffer(sess, orc, 0, f"long t={t}")
+        if t in (0, 5, 96, 97, 100):
+            ref = orc.attend(0, host(q), rows=rows)
+            ma, rel = check_attention(out[torch.from_numpy(rows).cuda()], ref, "bf16", f"long t={t}")
+            say(f"[bias long] t={t} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
+    assert orc.n_keys() == 46688
