@@ -14,6 +14,12 @@
 //                               place), read here as RAW slot t mod (Y+1) and
 //                               SUM slot f mod (W-Y) for the summarised frame f.
 //   "The rest of the model"     the clean pass rewrites the frame's entry.
+//   "Running for a long time"   the streaming sink: Z0's keys turned forward after
+//                               an eviction step once the gap reaches sink_gap.
+//   "Telling a summary from a pixel: level planes"
+//                               the temporal band and the level planes applied at
+//                               the write and to the query; the construction check.
+//   "Files", "Credits"          the optional recency bias on summary keys, by age.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
