@@ -258,3 +258,33 @@ def test_bias_long_horizon_sampled():
             ma, rel = check_attention(out[torch.from_numpy(rows).cuda()], ref, "bf16", f"long t={t}")
             say(f"[bias long] t={t} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
     assert orc.n_keys() == 46688
+
+
+@needs_gpu
+def test_bias_batch_beyond_one_launch():
+    """20 sessions in one sf_attend: 18 with a bias (two split-key launches of at most 16)
+    and 2 without (the stream-K read), at fill levels 0 .. 11."""
+    base = dict(hw=40, x=8, y=2, w=6, n_heads=2, head_dim=64, n_blocks=1, dtype="bf16", seed=51, v_scale=1.0)
+    g = so.Geometry.from_workload(base)
+    sessions, oracles, qs = [], [], []
+    for si in range(20):
+        biased = si not in (7, 13)
+        sess = sf.Session(sf.make_config(**dict(base, recency_bias=biased)))
+        orc = so.MemoryReplay(g)
+        if biased:
+            tab = table(base, si, 0)
+            sess.set_recency_bias(tab)
+            orc.set_recency_bias(tab.cpu().numpy())
+        for t in range(si % 12 + 1):
+            q, k, v = sf_inputs.frame_tensors(base, si, 0, t, device="cuda")
+            sess.step(0, t, q, k, v, out_like(base))
+            orc.step(t, {0: (host(k), host(v))})
+        sessions.append(sess)
+        oracles.append(orc)
+        qs.append(q)
+    outs = [out_like(base) for _ in sessions]
+    say("[bias batch 20]")
+    sf.attend_batch(sessions, 0, qs, outs)
+    torch.cuda.synchronize()
+    for si, (orc, q, out) in enumerate(zip(oracles, qs, outs)):
+        check_attention(out, orc.attend(0, host(q)), "bf16", f"s{si} keys={orc.n_keys()}")
