@@ -227,8 +227,9 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
  * every filled row of that session's block buffer, per head, for all R query rows; no mask.
  * scale <= 0 means 1/sqrt(head_dim).  Each session's block must hold its t_cur (SF_E_STATE
  * otherwise).  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
- * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One launch
- * (plus a combine launch when the key range is split) for the whole batch.
+ * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One attention
+ * launch per read path and per 16 sessions (plus a tail or combine launch where the keys are
+ * split).
  * [level] A session under SF_ROPE_LEVEL_* takes q unrotated: it is turned by that session's
  * t_cur (as sf_rope_rows does) into the session's own memory first, one launch per session.
  * [files], [credits] A session with recency_bias = 1 adds its bias (sf_set_recency_bias) to
