@@ -64,10 +64,66 @@ def parse():
                     help="skip the second leg (the same rollout with the library applying the temporal band)")
     ap.add_argument("--no-bias-leg", action="store_true",
                     help="skip the third leg (the same rollout with a recency bias on summary keys)")
+    ap.add_argument("--no-long-leg", action="store_true",
+                    help="skip the long-horizon leg (24 heads of 128, 46,688 keys per read)")
+    ap.add_argument("--no-batched-leg", action="store_true",
+                    help="skip the batched leg (8 sessions at fill levels 0..31, one sf_attend per block)")
+    ap.add_argument("--long-steps", type=int, default=4, help="timed frames of the long-horizon leg")
     return ap.parse_args()
 
 
-def cpu_baseline(wl, target_s, sink_gap):
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model name) of the host."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_long_block_step(rows_small=16, rows_large=64):
+    """The oracle's long-horizon block-step (24 heads of 128, 3,856 query rows, 46,688 keys)
+    timed on two subsamples of query rows; the read's fixed part (gathering the 46,688 keys in
+    fp64) and its per-row part are fitted from the two and extrapolated to all rows.  The
+    buffer is replayed to frame 100 with one frame's K/V written every frame (the read's cost
+    does not depend on the values)."""
+    import numpy as np
+    import sf_inputs
+    from oracle import sf_oracle as so
+    wl = dict(sf_inputs.WORKLOADS["long"], n_blocks=1)
+    g = so.Geometry.from_workload(wl)
+    orc = so.MemoryReplay(g)
+    q, k, v = (sf_inputs.to_host_bytes(x) for x in sf_inputs.frame_tensors(wl, 0, 0, 0))
+    for t in range(101):
+        orc.step(t, {0: (k, v)})
+    assert orc.n_keys() == 46688
+    timing = {}
+    for n in (rows_small, rows_large):
+        rows = np.arange(0, g.r, g.r // n)[:n]
+        start = time.perf_counter()
+        orc.attend(0, q, rows=rows)
+        timing[n] = time.perf_counter() - start
+    per_row = max((timing[rows_large] - timing[rows_small]) / (rows_large - rows_small), 0.0)
+    fixed = max(timing[rows_small] - per_row * rows_small, 0.0)
+    whole = fixed + per_row * g.r
+    return {"seconds_per_block_step": whole, "sample_rows": [rows_small, rows_large],
+            "sample_seconds": [round(timing[rows_small], 3), round(timing[rows_large], 3)],
+            "flop_per_block_step": 4.0 * g.r * 46688 * 24 * 128, "gflops": 4.0 * g.r * 46688 * 24 * 128 / whole / 1e9,
+            "note": f"fp64 attention of {rows_small} and {rows_large} of {g.r} query rows x 24 heads x 128 "
+                    f"against 46,688 keys; the fixed part (keys gathered in fp64, {fixed:.2f} s) plus "
+                    f"{g.r} x the per-row part ({per_row * 1e3:.1f} ms) extrapolate a whole block-step"}
+
+
+def cpu_baseline(wl, target_s, sink_gap, long_sample=True):
     """Times the oracle (fp64, numpy) on served block-steps at 6,528 keys; frames/s extrapolated to 28 blocks."""
     import numpy as np
     import sf_inputs
@@ -77,6 +133,7 @@ def cpu_baseline(wl, target_s, sink_gap):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    nproc, model = host_cpu()
     one = dict(wl, n_blocks=1)
     g = so.Geometry.from_workload(one)
     orc = so.MemoryReplay(g, sink_gap=sink_gap)
@@ -106,6 +163,9 @@ def cpu_baseline(wl, target_s, sink_gap):
                   f"query rows x 16 heads x 64), {el:.1f} s; frames/s extrapolated to 28 blocks",
         "seconds_per_block_step": per_block_step,
         "gflops": 4.0 * 1104 * 6528 * 16 * 64 / per_block_step / 1e9,
+        "threads_used": int(threads),
+        "host_logical_cpus": int(nproc),
+        "host_cpu_model": model,
     }
     # the same oracle on one core: one more block-step with the BLAS pool held to one thread
     try:
@@ -115,9 +175,12 @@ def cpu_baseline(wl, target_s, sink_gap):
             orc.step(t, {0: (k, v)})
             orc.attend(0, q)
             one_core = time.perf_counter() - s1
-        result["one_core"] = {"seconds_per_block_step": one_core, "frames_per_s": 1.0 / (one_core * wl["n_blocks"])}
+        result["one_core"] = {"seconds_per_block_step": one_core, "frames_per_s": 1.0 / (one_core * wl["n_blocks"]),
+                              "gflops": 4.0 * 1104 * 6528 * 16 * 64 / one_core / 1e9}
     except ImportError:
         pass
+    if long_sample:
+        result["long_horizon"] = cpu_long_block_step()
     return result
 
 
@@ -218,6 +281,162 @@ def bias_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup):
     }
 
 
+def long_leg(sf, sf_inputs, torch, steps, warmup=1):
+    """The long-horizon workload in steady state: 28 blocks, 24 heads of 128, 45x80 = 3,600 raw
+    + 256 summary tokens per record, Y = 4, W = 96, so every read has 46,688 keys.  The session
+    is filled through frame 99 with evictions and record writes only (no reads), then each timed
+    frame is the all-block eviction plus 28 x sf_step (separate record write, split-key read,
+    combine).  Inputs cycle through two seeded frames per block."""
+    wl = sf_inputs.WORKLOADS["long"]
+    nb, R, H, D, X = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"], wl["x"]
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    sess = sf.Session(sf.make_config(**wl), device=dev)
+    h = sess.handle
+    ring = [[sf_inputs.frame_tensors(wl, 0, b, i, device=dev) for b in range(nb)] for i in range(2)]
+    fill = 100
+    for t in range(fill):
+        if t >= 1:
+            sf.sf_evict(h, t, stream)
+        for b in range(nb):
+            _, k, v = ring[t % 2][b]
+            sf.sf_write_record(h, b, t, k, v, stream)
+    out = torch.empty((R, H, D), dtype=torch.float32, device=dev)
+    ptrs = [[(q.data_ptr(), k.data_ptr(), v.data_ptr()) for (q, k, v) in fr] for fr in ring]
+    lib, sptr, optr = sf._lib, stream.cuda_stream, out.data_ptr()
+    t = fill
+
+    def frames(n):
+        nonlocal t
+        for _ in range(n):
+            fr = ptrs[t % 2]
+            rc = 0
+            for b in range(nb):
+                rc |= lib.sf_step(h, b, t, fr[b][0], fr[b][1], fr[b][2], optr, ctypes.c_float(0.0), sptr)
+            if rc != 0:
+                raise RuntimeError("libsf call failed: " + sf.sf_last_error(h))
+            t += 1
+
+    frames(warmup)
+    torch.cuda.synchronize()
+    assert sess.view()["n_keys"] == 46688
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    frames(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    sf.sf_profile_enable(h, True)
+    frames(steps)
+    kt = sf.sf_kernel_times_read(h)
+    sf.sf_profile_enable(h, False)
+    sess.close()
+    avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
+    n_keys = 46688
+    flop = 4.0 * R * n_keys * H * D
+    call_ms = (kt["attend"][0] + kt["combine"][0]) / max(kt["attend"][1], 1)
+    evict_bytes = nb * 2 * 2 * X * H * D * 2
+    write_bytes = 2 * 2 * R * H * D * 2
+    return {
+        "workload": "long horizon, steady state: 28 blocks, 24 heads x 128, 45x80 raw + 256 summary tokens per "
+                    "record, Y=4, W=96, 46688 keys per read; step = eviction + 28 x sf_step; no sink",
+        "frames_per_s": round(steps / (ms * 1e-3), 3),
+        "ms_per_step": round(ms / steps, 3),
+        "attn_kernel": "attn_bf16_kernel<128, false> (split-key) + combine_kernel<128>",
+        "attn_flop_per_launch": flop,
+        "attn_avg_us": round(avg("attend") * 1e3, 2),
+        "attn_tflops": round(flop / (avg("attend") * 1e-3) / 1e12, 2),
+        "attn_frac_mfma": round(flop / (avg("attend") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "combine_avg_us": round(avg("combine") * 1e3, 2),
+        "attend_call_tflops": round(flop / (call_ms * 1e-3) / 1e12, 2),
+        "attend_call_frac_mfma": round(flop / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "evict_bytes": evict_bytes,
+        "evict_avg_us": round(avg("evict") * 1e3, 3),
+        "evict_gbps": round(evict_bytes / (avg("evict") * 1e-3) / 1e9, 1),
+        "evict_frac_hbm": round(evict_bytes / (avg("evict") * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "write_bytes": write_bytes,
+        "write_avg_us": round(avg("write") * 1e3, 3),
+        "write_gbps": round(write_bytes / (avg("write") * 1e-3) / 1e9, 1),
+        "attend_launches": kt["attend"][1], "evict_launches": kt["evict"][1],
+    }
+
+
+def batched_leg(sf, sf_inputs, torch, steps, warmup=2):
+    """Eight sessions at the served shape (28 blocks, 16 heads of 64) at fill levels t = 0, 1,
+    2, 3, 10, 23, 24, 31 (1,104 .. 6,528 keys, 35,424 in all per block); a step is one
+    batched sf_attend per block over all eight (one stream-K launch, tail, combine)."""
+    wl = sf_inputs.WORKLOADS["batched"]
+    nb, R, H, D = wl["n_blocks"], wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"]
+    levels = wl["frames"]
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    sessions = []
+    for si, t_end in enumerate(levels):
+        sess = sf.Session(sf.make_config(**wl), device=dev)
+        for t in range(t_end + 1):
+            if t >= 1:
+                sf.sf_evict(sess.handle, t, stream)
+            for b in range(nb):
+                _, k, v = sf_inputs.frame_tensors(wl, si, b, t, device=dev)
+                sf.sf_write_record(sess.handle, b, t, k, v, stream)
+        sessions.append(sess)
+    qs = [[sf_inputs.frame_tensors(wl, si, b, levels[si], device=dev)[0] for si in range(len(levels))]
+          for b in range(nb)]
+    outs = [torch.empty((R, H, D), dtype=torch.float32, device=dev) for _ in levels]
+    n = len(sessions)
+    hs = (ctypes.c_void_p * n)(*[s.handle for s in sessions])
+    qarr = [(ctypes.c_void_p * n)(*[q.data_ptr() for q in qs[b]]) for b in range(nb)]
+    oarr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    lib, sptr = sf._lib, stream.cuda_stream
+    keys = [s.view()["n_keys"] for s in sessions]
+    flop_block = sum(4.0 * R * kk * H * D for kk in keys)
+
+    def step():
+        rc = 0
+        for b in range(nb):
+            rc |= lib.sf_attend(hs, n, b, qarr[b], oarr, ctypes.c_float(0.0), sptr)
+        if rc != 0:
+            raise RuntimeError("libsf call failed: " + sf.sf_last_error(sessions[0].handle))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    # the batch's launches are traced through the first session's handle
+    sf.sf_profile_enable(sessions[0].handle, True)
+    for _ in range(steps):
+        step()
+    kt = sf.sf_kernel_times_read(sessions[0].handle)
+    sf.sf_profile_enable(sessions[0].handle, False)
+    for s in sessions:
+        s.close()
+    avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
+    call_ms = (kt["attend"][0] + kt["tail"][0] + kt["combine"][0]) / max(kt["attend"][1], 1)
+    return {
+        "workload": "8 sessions at the served shape, fill levels t = 0,1,2,3,10,23,24,31 (keys " +
+                    "/".join(str(k) for k in keys) + "); step = 28 x one batched sf_attend",
+        "keys_per_block": sum(keys),
+        "flop_per_block": flop_block,
+        "ms_per_step": round(ms / steps, 4),
+        "tflops": round(flop_block * nb / (ms * 1e-3) / 1e12, 2),
+        "attn_kernel": "attn_sk_kernel<false> (stream-K over all 8 sessions) + attn_tail_kernel + combine_sk_kernel",
+        "attn_avg_us": round(avg("attend") * 1e3, 3),
+        "attn_tflops": round(flop_block / (avg("attend") * 1e-3) / 1e12, 2),
+        "attn_frac_mfma": round(flop_block / (avg("attend") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "tail_avg_us": round(avg("tail") * 1e3, 3),
+        "combine_avg_us": round(avg("combine") * 1e3, 3),
+        "attend_call_us": round(call_ms * 1e3, 3),
+        "attend_call_frac_mfma": round(flop_block / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attend_launches": kt["attend"][1],
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,11 +471,7 @@ def main():
     # Pre-marshalled pointers and pre-created events keep the host ahead of the GPU.
     lib = sf._lib
     sptr = stream.cuda_stream
-    hs = (ctypes.c_void_p * 1)(h)
     ring_ptrs = [[(q.data_ptr(), k.data_ptr(), v.data_ptr()) for (q, k, v) in frame] for frame in ring]
-    qarr = [[(ctypes.c_void_p * 1)(p[0]) for p in frame] for frame in ring_ptrs]
-    oarr = (ctypes.c_void_p * 1)(out.data_ptr())
-
     optr = out.data_ptr()
 
     def one_frame(t):
@@ -361,6 +576,10 @@ def main():
         result["rope_leg"] = rope_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_bias_leg:
         result["bias_leg"] = bias_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
+    if not args.no_batched_leg:
+        result["batched_leg"] = batched_leg(sf, sf_inputs, torch, args.steps)
+    if not args.no_long_leg:
+        result["long_leg"] = long_leg(sf, sf_inputs, torch, args.long_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, sink_gap)
     print(json.dumps(result), flush=True)

@@ -348,6 +348,8 @@ class Session:
         if not isinstance(x, torch.Tensor) or x.dtype != want or not x.is_contiguous() or not x.is_cuda \
                 or x.numel() != shape[0] * shape[1] * shape[2]:
             raise SfError(SF_E_ARG, f"expected a contiguous {want} device tensor of {shape} elements")
+        if x.data_ptr() % 16:
+            raise SfError(SF_E_ARG, "device tensors must start on a 16-byte boundary")
         return x
 
     def write_record(self, block, t, k, v, stream=None):

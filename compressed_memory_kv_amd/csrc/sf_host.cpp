@@ -52,6 +52,11 @@ constexpr int64_t kMaxElemsPerBlockTensor = (int64_t)1 << 31;
 
 int64_t elem_bytes(int32_t dtype) { return dtype == SF_BF16 ? 2 : 4; }
 
+// Device tensors of a call are read and written in 16-byte vectors.
+bool aligned16(const void* a, const void* b = nullptr) {
+  return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
+}
+
 struct Geo {
   int64_t R, C, row_elems, tensor_bytes, block_stride, kv_bytes, scratch_off, scratch_bytes, qrot_off;
   int64_t bias_tab_off, bias_tab_bytes, bias_row_off, total;
@@ -397,9 +402,8 @@ sf_status check_write(sf_buffer* b, int32_t block, int64_t t, const void* k, con
   if (t < 0) return fail(b, SF_E_ARG, "negative frame id");
   if (c.max_frames > 0 && t >= c.max_frames) return fail(b, SF_E_RANGE, "frame id at or beyond max_frames");
   if (!b->dry && (!k || !v)) return fail(b, SF_E_ARG, "k or v is NULL");
-  if (!b->dry && c.rope_mode != SF_ROPE_CALLER &&
-      ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u))
-    return fail(b, SF_E_ARG, "k and v must be 16-byte aligned");
+  // every kernel that reads a record moves it in 16-byte vectors
+  if (!b->dry && !aligned16(k, v)) return fail(b, SF_E_ARG, "k and v must be 16-byte aligned");
   if (t == b->slots.t_cur) return SF_OK;  // rewrite of the current frame (clean pass)
   if (t != b->slots.t_cur + 1) return fail(b, SF_E_ORDER, "sf_write_record(t) needs t == t_cur or t_cur + 1");
   if (b->slots.t_cur >= 0 && !all_written(b, b->slots.t_cur))
@@ -463,6 +467,11 @@ sf_status check_attend_one(sf_buffer* b, int32_t block, bool after_write) {
   if (block < 0 || block >= b->cfg.n_blocks) return fail(b, SF_E_ARG, "block index out of range");
   if (!after_write && (b->slots.t_cur < 0 || b->written_at[block] != b->slots.t_cur))
     return fail(b, SF_E_STATE, "sf_attend: the block does not hold the current frame");
+  // Once the next frame's eviction step has run, the memory no longer holds what frame
+  // t_cur sees ([attends]): the leaving frame's summary has replaced an older one in SUM,
+  // and the sink may have turned Z0; the read waits for the next frame's write.
+  if (!after_write && b->slots.evicted_for == b->slots.t_cur + 1)
+    return fail(b, SF_E_STATE, "sf_attend: the next frame's eviction has run; write frame t_cur + 1 first");
   return SF_OK;
 }
 
@@ -690,8 +699,10 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
     }
     // SF_ATTN_SPLIT=n forces n key splits per (session, head, query tile) (tuning only:
     // results change only by rounding).
-    const char* split_env = std::getenv("SF_ATTN_SPLIT");
-    const int forced_split = split_env ? std::atoi(split_env) : 0;
+    static const int forced_split = [] {
+      const char* e = std::getenv("SF_ATTN_SPLIT");
+      return e ? std::atoi(e) : 0;
+    }();
     int64_t units = 0;
     bool any_bias = false;
     for (int i = 0; i < cnt; ++i) {
@@ -1007,8 +1018,7 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
     sf_status s = check_attend_one(b, block, false);
     if (s != SF_OK) return fail(bufs[0], s, b->err);
     if (!dry && (!q[i] || !out[i])) return fail(bufs[0], SF_E_ARG, "sf_attend: q or out pointer is NULL");
-    if (!dry && b->cfg.rope_mode != SF_ROPE_CALLER && (reinterpret_cast<uintptr_t>(q[i]) & 15u))
-      return fail(bufs[0], SF_E_ARG, "sf_attend: q must be 16-byte aligned under a rope mode");
+    if (!dry && !aligned16(q[i], out[i])) return fail(bufs[0], SF_E_ARG, "sf_attend: q and out must be 16-byte aligned");
   }
   for (int i = 0; i < n; ++i)
     if (take_injected(bufs[i])) return fail(bufs[0], SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
@@ -1027,8 +1037,7 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (!buf->dry && (!q || !out)) return fail(buf, SF_E_ARG, "sf_step: q or out is NULL");
-  if (!buf->dry && buf->cfg.rope_mode != SF_ROPE_CALLER && (reinterpret_cast<uintptr_t>(q) & 15u))
-    return fail(buf, SF_E_ARG, "sf_step: q must be 16-byte aligned under a rope mode");
+  if (!buf->dry && !aligned16(q, out)) return fail(buf, SF_E_ARG, "sf_step: q and out must be 16-byte aligned");
   if (!(scale == scale) || std::isinf(scale)) return fail(buf, SF_E_ARG, "sf_step: scale is not finite");
   // Validate every part before enqueueing anything.
   EvictPlan ep;
@@ -1042,6 +1051,8 @@ sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const
   if (s != SF_OK) return s;
   s = check_attend_one(buf, block, true);
   if (s != SF_OK) return s;
+  if (t == buf->slots.t_cur && buf->slots.evicted_for == t + 1)
+    return fail(buf, SF_E_STATE, "sf_step: rewrite of t_cur after the next frame's eviction; its read would be wrong");
   const Slots saved = buf->slots;
   const std::vector<int64_t> saved_written = buf->written_at;
   auto restore = [&](sf_status r) {

@@ -48,7 +48,8 @@
  * query; with the recency bias on, its table and the per-row biases of the
  * current frame).  The canonical K/V bytes are the first sf_kv_bytes(cfg) bytes.
  *
- * Tensors passed per call (device pointers, row-major, contiguous):
+ * Tensors passed per call (device pointers, row-major, contiguous, 16-byte aligned:
+ * the kernels move them in 16-byte vectors; a misaligned pointer is SF_E_ARG):
  *   q, k, v : [R][n_heads][head_dim] in the config dtype (fp32 or bf16)
  *   out     : [R][n_heads][head_dim] fp32
  *
@@ -225,8 +226,9 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
 /* [attends], [buffer] The dense read.  For each of n sessions (n <= SF_MAX_BATCH; equal
  * n_heads, head_dim and dtype; block < n_blocks in each): out[i] = softmax(scale * q K^T) V over
  * every filled row of that session's block buffer, per head, for all R query rows; no mask.
- * scale <= 0 means 1/sqrt(head_dim).  Each session's block must hold its t_cur (SF_E_STATE
- * otherwise).  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
+ * scale <= 0 means 1/sqrt(head_dim).  Each session's block must hold its t_cur, and the
+ * eviction step of t_cur + 1 must not have run yet (it replaces a summary frame t_cur still
+ * sees and may turn Z0): SF_E_STATE otherwise.  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
  * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One attention
  * launch per read path and per 16 sessions (plus a tail or combine launch where the keys are
  * split).
@@ -255,7 +257,8 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
 sf_status sf_set_recency_bias(sf_buffer* buf, const float* table, void* hip_stream);
 
 /* One block of one frame: sf_evict(t) if it is due and has not run, then sf_write_record,
- * then sf_attend of this session alone (q and k unrotated under SF_ROPE_LEVEL_*). */
+ * then sf_attend of this session alone (q and k unrotated under SF_ROPE_LEVEL_*).  A rewrite
+ * (t == t_cur) after sf_evict(t_cur + 1) is SF_E_STATE, as its read would be. */
 sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k,
                   const void* v, void* out, float scale, void* hip_stream);
 

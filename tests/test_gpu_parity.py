@@ -249,50 +249,61 @@ def _oracle_after(orc: so.MemoryReplay, t: int, block: int, k, v) -> so.MemoryRe
 def test_long_horizon_sampled():
     """Long-horizon workload (24 heads of 128, 46,688 keys): 28 blocks, 128 frames.
 
-    Blocks 0 and 27 get their own seeded inputs and are checked against the
-    oracle (changed rows every frame, whole buffers at three frames, attention
-    on sampled rows); blocks 1..26 reuse block 0's inputs, so their buffers
-    must equal block 0's bit for bit every frame."""
+    Blocks 0, 9, 18 and 27 get their own seeded inputs and are checked against the
+    oracle: every frame, the rows the frame changed (the record's rows and, from the
+    first eviction on, the SUM slot it filled); the whole buffers at three frames;
+    attention on sampled rows at seven frames.  The other blocks reuse block 0's inputs,
+    so their buffers must equal block 0's bit for bit every frame."""
     wl = sf_inputs.WORKLOADS["long"]
     g = so.Geometry.from_workload(wl)
     nb = wl["n_blocks"]
+    own = (0, 9, 18, 27)
     sess = new_session(wl)
-    orc = so.MemoryReplay(g, blocks=(0, 27))
+    orc = so.MemoryReplay(g, blocks=own)
     out = out_like(wl)
     att_at = {0, 1, 5, 6, 96, 97, 127}
+    att_blocks = {0, 27}
     full_buf_at = {6, 97, 127}
     rows = np.unique(np.concatenate([np.arange(0, g.r, 128), np.arange(g.hw, g.r, 8), [g.r - 1]]))
+    evictions = 0
     for t in wl["frames"]:
         say(f"[long] t={t}")
-        t0 = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
-        t27 = sf_inputs.frame_tensors(wl, 0, 27, t, device="cuda")
+        inputs = {b: sf_inputs.frame_tensors(wl, 0, b, t, device="cuda") for b in own}
         for b in range(nb):
-            q, k, v = t27 if b == 27 else t0
+            q, k, v = inputs[b if b in own else 0]
             sess.step(b, t, q, k, v, out)
-            if b in (0, 27) and t in att_at:
+            if b in att_blocks and t in att_at:
                 torch.cuda.synchronize()
                 tmp = _oracle_after(orc, t, b, host(k), host(v))
                 ref = tmp.attend(b, host(q), rows=rows)
                 ma, rel = check_attention(out[torch.from_numpy(rows).cuda()], ref, "bf16", f"long t={t} b{b}")
                 say(f"   b{b} keys={tmp.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
-        orc.step(t, {0: (host(t0[1]), host(t0[2])), 27: (host(t27[1]), host(t27[2]))})
+        moved = orc.step(t, {b: (host(inputs[b][1]), host(inputs[b][2])) for b in own})
         torch.cuda.synchronize()
         check_tables(sess, orc, f"long t={t}")
         k0, v0 = sess.kv(0)
-        for b in range(1, nb - 1):
+        for b in range(1, nb):
+            if b in own:
+                continue
             kb, vb = sess.kv(b)
             assert torch.equal(kb.view(torch.int16), k0.view(torch.int16)) and \
                 torch.equal(vb.view(torch.int16), v0.view(torch.int16)), f"long t={t}: block {b} != block 0"
+        evictions += moved is not None
         if t in full_buf_at:
-            for b in (0, 27):
+            for b in own:
                 check_buffer(sess, orc, b, f"long t={t} b{b}")
-        else:
-            # rows this frame changed: the record's rows and the summary slot it filled
-            for b in (0, 27):
-                kk, vv = sess.kv(b)
-                i = orc.index[b]
-                lo, hi = (0, g.r) if t == 0 else g.raw_rows(t % g.n_raw)
+            continue
+        # rows this frame changed: the record's rows and the SUM slot its eviction filled
+        changed = [(0, g.r) if t == 0 else g.raw_rows(t % g.n_raw)]
+        if moved is not None:
+            changed.append(g.sum_rows(moved[1]))
+        for b in own:
+            kk, vv = sess.kv(b)
+            i = orc.index[b]
+            for lo, hi in changed:
                 for name, gpu_t, ora in (("K", kk, orc.k), ("V", vv, orc.v)):
                     assert torch.equal(gpu_t[lo:hi].view(torch.int16),
-                                       torch.from_numpy(ora[i, lo:hi].view(np.int16)).cuda()), f"long t={t} b{b} {name}"
+                                       torch.from_numpy(ora[i, lo:hi].view(np.int16)).cuda()), \
+                        f"long t={t} b{b} {name} rows [{lo}, {hi})"
     assert orc.n_keys() == 46688
+    assert evictions == 122  # frames Y+2 = 6 .. 127 move a summary

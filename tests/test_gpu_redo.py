@@ -1,0 +1,309 @@
+"""GPU parity when scores spread far: the exact-max redo of the head_dim-64 stream-K read,
+the caller-given softmax scale, and the same inputs through the split-key and fp32 reads.
+
+Model card "GTA world model: weights and inference code", section "One buffer, no mask":
+the read is one dense softmax over every filled row, exact whatever the scores are.  The
+bf16 head_dim-64 kernel takes one softmax reference per key stream (the max of the
+stream's first 32 scores) and redoes a piece with exact maxima when some probability
+against that reference exceeds 2^40.  With N(0,1) inputs at scale 1/sqrt(d) that never
+happens, so these tests build buffers where it must:
+
+  For every 128-row query unit (head h, query tile qt) one designated query row i is
+  chosen, and in every full 64-key tile of the flattened key sequence the key at offset
+  32 + qt (the tile's second half) is set to beta_tau * q[i, h] (rounded to bf16).  Every
+  key stream of the kernel starts at a tile boundary and takes its reference from that
+  tile's first 32 keys, which are plain N(0,1) keys; the planted key in the same tile's
+  second half then scores far above the reference for query i.
+
+Before any launch the test proves, from the oracle's fp64 scores of the final buffer
+bytes, that in every tile the second half's max exceeds the first half's max by at
+least 45 log2 units for the designated query of every unit: so in every piece of every
+workgroup some probability exceeds 2^40 and the redo runs.  beta_tau cycles through
+beta * (1, 1.25, 1.5, 1.75, 2) with the tile index, so the planted scores also climb by
+about 12 nats from tile to tile, which moves the split-key kernel's reference (it
+recomputes a tile against a new max when a tile's sum passes 2^15).
+
+Outputs are compared element by element with the oracle at the bf16 bar (max-abs 2e-2,
+relative L2 1e-2) and the fp32 bar (1e-5) for the fp32 read.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import sf_inputs
+from oracle import sf_oracle as so
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import compressed_memory_kv_amd as sf
+else:  # collected on a CPU-only machine: every test here is skipped
+    sf = None
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
+
+TOL = {"f32": dict(max_abs=1e-5, rel_l2=1e-5), "bf16": dict(max_abs=2e-2, rel_l2=1e-2)}
+TILE = 64          # keys per tile of the stream-K read
+UNIT_ROWS = 128    # query rows per unit
+MARGIN_LOG2 = 45.0  # proven spread, log2 units; the redo threshold is 40
+BETA = 10.0
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def host(x):
+    return sf_inputs.to_host_bytes(x)
+
+
+def check_attention(got, ref, dtype, what):
+    g = got.detach().double().cpu().numpy()
+    err = np.abs(g - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    assert max_abs <= TOL[dtype]["max_abs"], f"{what}: max-abs {max_abs:.3e} > {TOL[dtype]['max_abs']}"
+    assert rel <= TOL[dtype]["rel_l2"], f"{what}: rel-L2 {rel:.3e} > {TOL[dtype]['rel_l2']}"
+    say(f"   {what}: max_abs={max_abs:.2e} rel_l2={rel:.2e}")
+
+
+def flat_rows(segments, cut=None):
+    """Buffer row of each flattened key: the readable segments in ascending order; with
+    cut = (lo, hi), the rows of the record being written by the same call (sf_step's
+    read of a record from its source) are taken out and visited last."""
+    rows = np.concatenate([np.arange(b, b + n) for b, n in segments]) if segments else np.zeros(0, np.int64)
+    if cut is None:
+        return rows
+    lo, hi = cut
+    keep = rows[(rows < lo) | (rows >= hi)]
+    return np.concatenate([keep, np.arange(lo, hi)])
+
+
+def bf16_of(x: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to bf16 (nearest even), as uint16 bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def designated(r: int):
+    """One query row inside each 128-row unit."""
+    return [min(UNIT_ROWS * qt + 7, r - 1) for qt in range((r + UNIT_ROWS - 1) // UNIT_ROWS)]
+
+
+def plant_keys(k_rows: np.ndarray, q_bits: np.ndarray, order: np.ndarray, beta: float, dtype: str):
+    """Sets the planted keys in k_rows ([C][H][d] storage, indexed by buffer row) in place.
+    Returns the buffer rows changed."""
+    r = q_bits.shape[0]
+    qf = so.stored_to_f64(q_bits)
+    rows_changed = []
+    for tau in range(len(order) // TILE):
+        b = beta * (1.0 + 0.25 * (tau % 5))
+        for qt, i in enumerate(designated(r)):
+            row = int(order[TILE * tau + TILE // 2 + qt])
+            val = b * qf[i]                                   # [H][d]
+            k_rows[row] = bf16_of(val) if dtype == "bf16" else val.astype(np.float32)
+            rows_changed.append(row)
+    return np.asarray(rows_changed, dtype=np.int64)
+
+
+def prove_redo(k_rows: np.ndarray, q_bits: np.ndarray, order: np.ndarray, scale: float):
+    """Asserts that in every full tile the designated query of every unit scores, in the
+    tile's second half, at least MARGIN_LOG2 above the max of its first half."""
+    h_n = q_bits.shape[1]
+    qf = so.stored_to_f64(q_bits)
+    kf = so.stored_to_f64(k_rows[order[: len(order) // TILE * TILE]])  # [keys][H][d]
+    worst = np.inf
+    for h in range(h_n):
+        for i in designated(q_bits.shape[0]):
+            s = (kf[:, h, :] @ qf[i, h, :]) * scale * np.log2(np.e)
+            s = s.reshape(-1, TILE)
+            spread = s[:, TILE // 2:].max(axis=1) - s[:, : TILE // 2].max(axis=1)
+            worst = min(worst, float(spread.min()))
+    assert worst >= MARGIN_LOG2, f"planted spread {worst:.1f} log2 units does not force the redo"
+    return worst
+
+
+def replay(wl, t_end, *, session=0, sess_kw=None, orc_kw=None):
+    """A one-block session and its oracle stepped through frames 0..t_end (sf_step)."""
+    g = so.Geometry.from_workload(wl)
+    sess = sf.Session(sf.make_config(**dict(wl, **(sess_kw or {}))))
+    orc = so.MemoryReplay(g, **(orc_kw or {}))
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    for t in range(t_end + 1):
+        q, k, v = sf_inputs.frame_tensors(wl, session, 0, t, device="cuda")
+        sess.step(0, t, q, k, v, out)
+        orc.step(t, {0: (host(k), host(v))})
+    torch.cuda.synchronize()
+    return sess, orc, g
+
+
+def plant_buffer(sess, orc, q_bits, order, beta, dtype):
+    """Plants into the session's K (device) and the oracle's K, the same values."""
+    k_rows = orc.k[orc.index[0]]
+    changed = plant_keys(k_rows, q_bits, order, beta, dtype)
+    kk, _ = sess.kv(0)
+    rows = torch.from_numpy(np.unique(changed)).cuda()
+    src = k_rows[np.unique(changed)]
+    if dtype == "bf16":
+        kk[rows] = torch.from_numpy(src.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        kk[rows] = torch.from_numpy(src).cuda()
+    torch.cuda.synchronize()
+    return k_rows
+
+
+SERVED = sf_inputs.WORKLOADS["served1"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("scale", [0.0, 0.25])
+def test_redo_served_attend(scale):
+    """Served shape at frame 31 (6,528 keys, 102 full tiles, one segment), sf_attend:
+    attn_sk_kernel redoes every piece; every output row against the oracle."""
+    say(f"[redo served attend] scale={scale}")
+    sess, orc, g = replay(SERVED, 31)
+    q, _, _ = sf_inputs.frame_tensors(SERVED, 9, 0, 31, device="cuda")
+    qb = host(q)
+    order = flat_rows(orc.readable_segments())
+    assert len(order) == 6528
+    k_rows = plant_buffer(sess, orc, qb, order, BETA, "bf16")
+    sc = scale if scale > 0 else so.default_scale(64)
+    say(f"   proven spread {prove_redo(k_rows, qb, order, sc):.1f} log2 units")
+    out = torch.empty(sf_inputs.record_shape(SERVED), dtype=torch.float32, device="cuda")
+    sess.attend(0, q, out, scale=scale)
+    torch.cuda.synchronize()
+    check_attention(out, orc.attend(0, qb, scale=scale), "bf16", f"served attend scale={scale}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("scale", [0.0, 0.25])
+def test_redo_served_step_reads_record_from_source(scale):
+    """Served shape, sf_step at frame 31: the read that takes the new record's keys from
+    the caller's tensor (visited after the buffer's other rows) and copies the record in
+    its combine launch.  Keys planted in the buffer and in the caller's k; the redo is
+    proven in that visiting order; output and buffer bytes against the oracle."""
+    say(f"[redo served step] scale={scale}")
+    t = 31
+    sess, orc, g = replay(SERVED, t - 1)
+    q, k, v = sf_inputs.frame_tensors(SERVED, 0, 0, t, device="cuda")
+    qb, kb, vb = host(q), host(k), host(v)
+    sess.evict(t)          # the eviction first, so the rows planted below are what the read sees
+    orc.evict(t)
+    torch.cuda.synchronize()
+    lo, hi = g.raw_rows(t % g.n_raw)
+    # the buffer once the record is in its RAW slot (the slot was readable before: the
+    # segments do not change); the read visits the other rows, then the record's
+    k_all = orc.k[orc.index[0]].copy()
+    k_all[lo:hi] = kb
+    order = flat_rows(orc.readable_segments(), cut=(lo, hi))
+    assert len(order) == 6528
+    changed = np.unique(plant_keys(k_all, qb, order, BETA, "bf16"))
+    sc = scale if scale > 0 else so.default_scale(64)
+    say(f"   proven spread {prove_redo(k_all, qb, order, sc):.1f} log2 units")
+    in_buf = changed[(changed < lo) | (changed >= hi)]
+    orc.k[orc.index[0], in_buf] = k_all[in_buf]
+    kk, _ = sess.kv(0)
+    kk[torch.from_numpy(in_buf).cuda()] = torch.from_numpy(k_all[in_buf].view(np.int16)).cuda().view(torch.bfloat16)
+    k_planted = torch.from_numpy(k_all[lo:hi].view(np.int16)).cuda().view(torch.bfloat16).contiguous()
+    out = torch.empty(sf_inputs.record_shape(SERVED), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    sess.step(0, t, q, k_planted, v, out, scale=scale)
+    orc.write(0, t, k_all[lo:hi], vb)
+    torch.cuda.synchronize()
+    check_attention(out, orc.attend(0, qb, scale=scale), "bf16", f"served step scale={scale}")
+    kk, vv = sess.kv(0)
+    assert torch.equal(kk.view(torch.int16).cpu(), torch.from_numpy(orc.k[0].view(np.int16)))
+    assert torch.equal(vv.view(torch.int16).cpu(), torch.from_numpy(orc.v[0].view(np.int16)))
+
+
+@needs_gpu
+def test_redo_batched_with_tails():
+    """Eight sessions at fill levels 0, 1, 2, 3, 10, 23, 24, 31 (1,104 to 6,528 keys; at 0,
+    1, 2 and 10 the keys leave a tail of 16 to 48 past the last full tile, read by the
+    tail kernel) in one batched stream-K launch at a caller scale of 0.25; every session
+    planted in its own visiting order."""
+    levels = [0, 1, 2, 3, 10, 23, 24, 31]
+    wl = dict(SERVED, seed=11)
+    scale = 0.25
+    sessions, oracles, qs, qbits = [], [], [], []
+    for si, t_end in enumerate(levels):
+        say(f"[redo batched] session {si} to t={t_end}")
+        sess, orc, g = replay(wl, t_end, session=si)
+        q, _, _ = sf_inputs.frame_tensors(wl, si, 0, t_end, device="cuda")
+        qb = host(q)
+        order = flat_rows(orc.readable_segments())
+        if len(order) >= TILE:
+            k_rows = plant_buffer(sess, orc, qb, order, BETA, "bf16")
+            prove_redo(k_rows, qb, order, scale)
+        sessions.append(sess)
+        oracles.append(orc)
+        qs.append(q)
+        qbits.append(qb)
+    assert [o.n_keys() % TILE for o in oracles][:3] == [16, 32, 48]
+    outs = [torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda") for _ in levels]
+    sf.attend_batch(sessions, 0, qs, outs, scale=scale)
+    torch.cuda.synchronize()
+    for si, orc in enumerate(oracles):
+        check_attention(outs[si], orc.attend(0, qbits[si], scale=scale), "bf16",
+                        f"batched s{si} t={levels[si]} keys={orc.n_keys()}")
+
+
+@needs_gpu
+def test_redo_inputs_through_split_key_read():
+    """The served frame-31 buffer with the same planted keys through the split-key bf16
+    kernel (a session with a recency bias whose table is all zeros, so the read is the
+    plain one), at a caller scale of 0.25."""
+    q, _, _ = sf_inputs.frame_tensors(SERVED, 9, 0, 31, device="cuda")
+    qb = host(q)
+    say("[redo split-key bf16]")
+    sess, orc, g = replay(SERVED, 31, sess_kw=dict(recency_bias=True))
+    sess.set_recency_bias(torch.zeros((SERVED["n_heads"], SERVED["w"] + 1), dtype=torch.float32, device="cuda"))
+    order = flat_rows(orc.readable_segments())
+    plant_buffer(sess, orc, qb, order, BETA, "bf16")
+    out = torch.empty(sf_inputs.record_shape(SERVED), dtype=torch.float32, device="cuda")
+    sess.attend(0, q, out, scale=0.25)
+    torch.cuda.synchronize()
+    check_attention(out, orc.attend(0, qb, scale=0.25), "bf16", "split-key bf16 scale=0.25")
+
+
+@needs_gpu
+@pytest.mark.parametrize("beta", [1.0, 2.0])
+def test_redo_construction_through_fp32_read(beta):
+    """The fp32 read (exact online softmax, no redo) with the same planted construction, on
+    a 608-key geometry (2 heads of 64, 136-row records, 9 full tiles and a ragged one) at
+    the fp32 bar of 1e-5.  That bar belongs to the short fp32 workloads: at the served
+    shape the read sums 6,528 terms in fp32 and measured 2.1e-5, which is what a CPU
+    simulation of the same fp32 accumulation order gives (9e-6 on one head of 16)."""
+    wl = dict(hw=120, x=16, y=2, w=6, n_heads=2, head_dim=64, n_blocks=1, dtype="f32", seed=13, v_scale=1.0)
+    sess, orc, g = replay(wl, 9)
+    q, _, _ = sf_inputs.frame_tensors(wl, 2, 0, 9, device="cuda")
+    qb = host(q)
+    order = flat_rows(orc.readable_segments())
+    assert len(order) == 608
+    plant_buffer(sess, orc, qb, order, beta, "f32")
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    sess.attend(0, q, out)
+    torch.cuda.synchronize()
+    check_attention(out, orc.attend(0, qb), "f32", f"fp32 read beta={beta}")
+
+
+@needs_gpu
+def test_redo_head_dim_128_with_tail():
+    """head_dim 128 (the split-key kernel's other width): 4 heads, 560-row records, 2,600
+    keys once full (40 full tiles and a ragged tile of 40 keys), planted the same way."""
+    wl = dict(hw=500, x=60, y=2, w=8, n_heads=4, head_dim=128, n_blocks=1, dtype="bf16", seed=12, v_scale=1.0)
+    sess, orc, g = replay(wl, 12)
+    q, _, _ = sf_inputs.frame_tensors(wl, 3, 0, 12, device="cuda")
+    qb = host(q)
+    order = flat_rows(orc.readable_segments())
+    assert len(order) == 2600
+    k_rows = plant_buffer(sess, orc, qb, order, BETA, "bf16")
+    prove_redo(k_rows, qb, order, so.default_scale(128))
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    sess.attend(0, q, out)
+    torch.cuda.synchronize()
+    check_attention(out, orc.attend(0, qb), "bf16", "head_dim 128")

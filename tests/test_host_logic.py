@@ -193,6 +193,28 @@ def test_advance_needs_every_block():
     sf.sf_attend([h], 0, None, None)
 
 
+def test_attend_refused_after_next_eviction():
+    """[attends]: once sf_evict(t_cur + 1) has run, SUM no longer holds what frame t_cur sees
+    (the leaving frame's summary replaced an older one), so a read of t_cur is SF_E_STATE, and
+    so is an sf_step rewrite of t_cur; the write of t_cur + 1 then reopens reads."""
+    s, wl = dry_session("tiny", hw=4, x=2, y=2, w=6, n_blocks=1)
+    h = s.handle
+    for t in range(10):
+        advance(s, wl, t)
+    sf.sf_attend([h], 0, None, None)
+    sf.sf_evict(h, 10)
+    v = s.view()
+    assert v["t_cur"] == 9 and v["evicted_for"] == 10
+    # frame 7's summary now sits in SUM beside its raw rows: frame 9 would count it twice
+    assert 7 in v["raw_frame"] and 7 in v["sum_frame"] and 3 not in v["sum_frame"]
+    expect(sf.SF_E_STATE, sf.sf_attend, [h], 0, None, None)
+    expect(sf.SF_E_STATE, sf.sf_step, h, 0, 9, None, None, None, None)
+    sf.sf_write_record(h, 0, 9, None, None)          # a rewrite of frame 9's rows is harmless
+    assert s.view() == v
+    sf.sf_write_record(h, 0, 10, None, None)
+    sf.sf_attend([h], 0, None, None)
+
+
 def test_batched_attend_checks():
     a, wl = dry_session("odd")
     b, _ = dry_session("odd")
