@@ -893,8 +893,8 @@ sf_status sf_record_slot(sf_buffer* buf, int32_t block, int64_t t, void** k_rows
   if (buf->cfg.rope_mode != SF_ROPE_CALLER)
     return fail(buf, SF_E_UNSUPPORTED, "sf_record_slot: rows are stored as given; not under a rope mode");
   // the same checks as a write; the pointers stand in for the caller's data
-  const char dummy = 0;
-  sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
+  alignas(16) static const char stand_in[16] = {};
+  sf_status s = check_write(buf, block, t, stand_in, stand_in, false);
   if (s != SF_OK) return s;
   if (buf->dry) {
     *k_rows = *v_rows = nullptr;
@@ -911,8 +911,8 @@ sf_status sf_commit_record(sf_buffer* buf, int32_t block, int64_t t) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   if (buf->cfg.rope_mode != SF_ROPE_CALLER)
     return fail(buf, SF_E_UNSUPPORTED, "sf_commit_record: rows are stored as given; not under a rope mode");
-  const char dummy = 0;
-  sf_status s = check_write(buf, block, t, &dummy, &dummy, false);
+  alignas(16) static const char stand_in[16] = {};
+  sf_status s = check_write(buf, block, t, stand_in, stand_in, false);
   if (s != SF_OK) return s;
   write_state(buf, block, t);
   return SF_OK;
