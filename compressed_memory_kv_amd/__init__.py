@@ -36,7 +36,7 @@ EXPORTED = (
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
     "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import", "sf_rope_rows",
-    "sf_set_recency_bias",
+    "sf_set_recency_bias", "sf_attend_static_scratch",
 )
 (SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_ROPE, SF_K_BIAS,
  SF_K_KINDS) = range(10)
@@ -92,6 +92,8 @@ _sig = {
     "sf_state_import": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "sf_rope_rows": (ctypes.c_int, [_CFG, ctypes.c_int64, _P, _P, _P]),
     "sf_set_recency_bias": (ctypes.c_int, [_P, _P, _P]),
+    "sf_attend_static_scratch": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.c_float, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -189,6 +191,14 @@ def sf_attend(handles, block: int, q, out, scale: float = 0.0, stream=None) -> N
     qs = (_P * n)(*[_ptr(x) for x in q]) if q is not None else None
     os_ = (_P * n)(*[_ptr(x) for x in out]) if out is not None else None
     _check(_lib.sf_attend(hs, n, block, qs, os_, scale, _stream(stream)), None)
+
+
+def sf_attend_static_scratch(handles, block: int, q, out, scale: float = 0.0, stream=None) -> None:
+    n = len(handles)
+    hs = (_P * n)(*handles)
+    qs = (_P * n)(*[_ptr(x) for x in q]) if q is not None else None
+    os_ = (_P * n)(*[_ptr(x) for x in out]) if out is not None else None
+    _check(_lib.sf_attend_static_scratch(hs, n, block, qs, os_, scale, _stream(stream)), None)
 
 
 def sf_step(handle: int, block: int, t: int, q, k, v, out, scale: float = 0.0, stream=None) -> None:

@@ -475,13 +475,39 @@ sf_status check_attend_one(sf_buffer* b, int32_t block, bool after_write) {
   return SF_OK;
 }
 
+// Device scratch a read takes from one region instead of the sessions' own memory: the
+// partial results of split reads and the turned queries of rope modes, laid out one after
+// the other (256-byte aligned).  NULL: every session uses its own scratch region.
+// A planning arena (plan = true) only adds up the bytes: the reads it is passed to lay
+// out their scratch and launch nothing.
+struct Arena {
+  char* base;
+  size_t cap;
+  size_t used;
+  bool plan;
+  char* take(size_t bytes) {
+    const size_t need = (bytes + 255) / 256 * 256;
+    if (need > cap - used) return nullptr;
+    char* p = base + used;
+    used += need;
+    return p;
+  }
+};
+bool planning(const Arena* a) { return a && a->plan; }
+
 // [level] A query under a rope mode, turned by the session's current frame into the
-// session's own memory; *qs is then what the read uses.  Other sessions: *qs = q.
-sf_status stage_query(sf_buffer* b, const void* q, const void** qs, hipStream_t st) {
+// session's own memory (or the arena); *qs is then what the read uses.  Other sessions:
+// *qs = q.
+sf_status stage_query(sf_buffer* b, const void* q, const void** qs, hipStream_t st, Arena* arena = nullptr) {
   *qs = q;
   const sf_config& c = b->cfg;
   if (c.rope_mode == SF_ROPE_CALLER || b->dry) return SF_OK;
   char* dst = b->mem + b->geo.qrot_off;
+  if (arena) {
+    dst = arena->take((size_t)(b->geo.R * b->geo.row_elems * elem_bytes(c.dtype)));
+    if (!dst) return fail(b, SF_E_UNSUPPORTED, "sf_attend_static_scratch: the static scratch array is too small");
+    if (arena->plan) return SF_OK;
+  }
   TraceScope ts(b->trace, SF_K_ROPE, st);
   const sf::RopeJob job = {nullptr, nullptr, dst, nullptr, nullptr, q};
   hipError_t e = sf::launch_rope_rows(job, (int)b->geo.R, c.hw, c.n_heads, c.head_dim, c.dtype == SF_BF16,
@@ -571,7 +597,8 @@ Segs cut_record(const Segs& sg, int64_t row0, int64_t rows, int* rec_seg) {
 }
 
 sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
-                            void* const* out, float scale_log2, hipStream_t st, const RecWrite* rec = nullptr) {
+                            void* const* out, float scale_log2, hipStream_t st, const RecWrite* rec = nullptr,
+                            Arena* arena = nullptr) {
   sf_buffer* b0 = bufs[0];
   const int H = b0->cfg.n_heads;
   for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
@@ -613,10 +640,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.qtiles = (int32_t)((b->geo.R + sf::kSkRows - 1) / sf::kSkRows);
       s.ntiles = (int32_t)(sg.keys / sf::kSkKeys);
       any_tail = any_tail || (sg.keys % sf::kSkKeys) != 0;
-      s.ppu = sf::sk_pieces_per_unit(b->geo.C);
       const int64_t units = (int64_t)H * s.qtiles;
-      s.part_o = reinterpret_cast<float*>(b->mem + b->geo.scratch_off);
-      s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
       s.it_begin = (int32_t)iters;
       iters += units * s.ntiles;
       units_total += units;
@@ -629,6 +653,31 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     if (G >= 8) G -= G % 8;
     a.n_wg = (int32_t)G;
     a.n_iters = (int32_t)iters;
+    // Partial-result slots per unit: every workgroup range holds at least floor(N / G)
+    // tiles, so a unit of ntiles tiles meets at most ceil(ntiles / that) + 1 ranges; one
+    // more slot for the tail.  G <= N / kSkMinRange makes floor(N / G) >= kSkMinRange (or
+    // G = 1 and one range holds every tile), so this never exceeds the capacity bound the
+    // session's own scratch region is sized for.
+    const int64_t per_wg = iters / G > 0 ? iters / G : 1;
+    for (int i = 0; i < cnt; ++i) {
+      sf_buffer* b = bufs[first + i];
+      sf::SkSession& s = a.s[i];
+      s.ppu = (int32_t)((s.ntiles + per_wg - 1) / per_wg + 2);
+      if (s.ppu > sf::sk_pieces_per_unit(b->geo.C))
+        return fail(b0, SF_E_UNSUPPORTED, "internal: stream-K partial slots exceed the session's scratch bound");
+      const int64_t units = (int64_t)H * s.qtiles;
+      const size_t bytes = (size_t)units * s.ppu * sf::kSkRows * (64 + 2) * sizeof(float);
+      char* base = b->mem + b->geo.scratch_off;
+      if (arena) {
+        base = arena->take(bytes);
+        if (!base)
+          return fail(b0, SF_E_UNSUPPORTED, "sf_attend_static_scratch: the read needs more scratch than the static "
+                                            "array holds (" + std::to_string(SF_STATIC_SCRATCH_BYTES) + " bytes)");
+      }
+      s.part_o = reinterpret_cast<float*>(base);
+      s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
+    }
+    if (planning(arena)) continue;
     hipError_t e = hipSuccess;
     if (iters > 0) {
       TraceScope ts(b0->trace, SF_K_ATTEND, st);
@@ -651,7 +700,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
 
 // The split-key (bf16) or fp32 read; sessions with a recency bias get their per-row biases.
 sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
-                               void* const* out, float scale_log2, hipStream_t st) {
+                               void* const* out, float scale_log2, hipStream_t st, Arena* arena = nullptr) {
   sf_buffer* b0 = bufs[0];
   const sf_config& c0 = b0->cfg;
   for (int first = 0; first < n; first += sf::kMaxLaunchSessions) {
@@ -709,7 +758,7 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
       sf_buffer* b = bufs[first + i];
       sf::AttnSession& s = a.s[i];
       if (b->cfg.recency_bias) {
-        sf_status r = refresh_bias(b, st);
+        sf_status r = planning(arena) ? SF_OK : refresh_bias(b, st);
         if (r != SF_OK) return fail(b0, r, b->err);
         s.bias = reinterpret_cast<const float*>(b->mem + b->geo.bias_row_off);
         s.bias_stride = (int32_t)b->geo.C;
@@ -740,12 +789,22 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
         if (split < 1) split = 1;
       }
       s.split = (int32_t)split;
+      if (arena && split > 1) {
+        const size_t slice = (size_t)b->geo.R * c0.n_heads;
+        char* base = arena->take((size_t)split * slice * (c0.head_dim + 2) * sizeof(float));
+        if (!base)
+          return fail(b0, SF_E_UNSUPPORTED, "sf_attend_static_scratch: the read needs more scratch than the static "
+                                            "array holds (" + std::to_string(SF_STATIC_SCRATCH_BYTES) + " bytes)");
+        s.part_o = reinterpret_cast<float*>(base);
+        s.part_ml = s.part_o + (size_t)split * slice * c0.head_dim;
+      }
       s.unit_begin = (int32_t)units;
       units += (int64_t)s.qtiles * c0.n_heads * split;
     }
     (void)base_units;
     if (units >= ((int64_t)1 << 30)) return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
     a.total_units = (int32_t)units;
+    if (planning(arena)) continue;
     hipError_t e;
     {
       TraceScope ts(b0->trace, SF_K_ATTEND, st);
@@ -762,11 +821,12 @@ sf_status enqueue_attend_split(sf_buffer* const* bufs, int32_t n, int32_t block,
 }
 
 sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
-                         float scale, hipStream_t st) {
+                         float scale, hipStream_t st, Arena* arena = nullptr) {
   const sf_config& c0 = bufs[0]->cfg;
   const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c0.head_dim);
   const float scale_log2 = sc * 1.4426950408889634f;
-  if (c0.dtype != SF_BF16 || c0.head_dim != 64) return enqueue_attend_split(bufs, n, block, q, out, scale_log2, st);
+  if (c0.dtype != SF_BF16 || c0.head_dim != 64)
+    return enqueue_attend_split(bufs, n, block, q, out, scale_log2, st, arena);
   // bf16 head_dim 64: the stream-K kernel, except for sessions with a recency bias
   sf_buffer* gb[2][SF_MAX_BATCH];
   const void* gq[2][SF_MAX_BATCH];
@@ -780,11 +840,11 @@ sf_status enqueue_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const
     ++cnt[k];
   }
   if (cnt[0] > 0) {
-    sf_status s = enqueue_attend_sk(gb[0], cnt[0], block, gq[0], go[0], scale_log2, st);
+    sf_status s = enqueue_attend_sk(gb[0], cnt[0], block, gq[0], go[0], scale_log2, st, nullptr, arena);
     if (s != SF_OK) return s;
   }
   if (cnt[1] == 0) return SF_OK;
-  return enqueue_attend_split(gb[1], cnt[1], block, gq[1], go[1], scale_log2, st);
+  return enqueue_attend_split(gb[1], cnt[1], block, gq[1], go[1], scale_log2, st, arena);
 }
 
 void fill_view(const sf_config& c, const Geo& g, const Slots& s, int32_t blocks_written, sf_view* v) {
@@ -999,8 +1059,39 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream) {
   return apply_evict(buf, t, p, static_cast<hipStream_t>(hip_stream));
 }
 
-sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
-                    float scale, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The library's own device scratch for sf_attend_static_scratch: one array per device that
+// holds the library, reached through the address hipGetSymbolAddress gives for the device
+// (the array's name in host code is a host-side stand-in, not a device address).
+static __device__ __align__(256) char scratch[SF_STATIC_SCRATCH_BYTES];
+
+// Address of the current device's copy of the array, looked up once per device.
+sf_status static_scratch(char** out) {
+  static std::atomic<char*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, SF_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(nullptr, SF_E_UNSUPPORTED, "sf_attend_static_scratch: device index >= 64");
+  char* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !addr)
+      return fail(nullptr, SF_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    p = static_cast<char*>(addr);
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SF_OK;
+}
+
+// sf_attend; with static_scratch_arena, the read's scratch comes from this device's copy of
+// the static array instead of the sessions' memory.
+sf_status attend_impl(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
+                      float scale, void* hip_stream, bool static_scratch_arena) {
   if (!bufs || n < 1 || n > SF_MAX_BATCH) return fail(nullptr, SF_E_ARG, "sf_attend: need 1 <= n <= SF_MAX_BATCH");
   if (!bufs[0]) return fail(nullptr, SF_E_ARG, "sf_attend: NULL buffer");
   const sf_config& c0 = bufs[0]->cfg;
@@ -1023,13 +1114,46 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
   for (int i = 0; i < n; ++i)
     if (take_injected(bufs[i])) return fail(bufs[0], SF_E_HIP, "injected launch failure (sf_debug_fail_next_launch)");
   if (dry) return SF_OK;
+  Arena arena = {nullptr, SF_STATIC_SCRATCH_BYTES, 0, false};
+  Arena* ap = nullptr;
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const void* qs[SF_MAX_BATCH];
+  if (static_scratch_arena) {
+    // Lay the whole read's scratch out first, so a read that does not fit enqueues nothing.
+    Arena plan = {reinterpret_cast<char*>(static_cast<uintptr_t>(256)), SIZE_MAX / 2, 0, true};
+    for (int i = 0; i < n; ++i) {
+      sf_status s = stage_query(bufs[i], q[i], &qs[i], st, &plan);
+      if (s != SF_OK) return fail(bufs[0], s, bufs[i]->err);
+    }
+    sf_status s = enqueue_attend(bufs, n, block, qs, out, scale, st, &plan);
+    if (s != SF_OK) return s;
+    if (plan.used > SF_STATIC_SCRATCH_BYTES)
+      return fail(bufs[0], SF_E_UNSUPPORTED, "sf_attend_static_scratch: the read needs " + std::to_string(plan.used) +
+                                                 " bytes of scratch; the static array holds " +
+                                                 std::to_string(SF_STATIC_SCRATCH_BYTES));
+    s = static_scratch(&arena.base);
+    if (s != SF_OK) return fail(bufs[0], s, g_thread_error);
+    ap = &arena;
+  }
   for (int i = 0; i < n; ++i) {
-    sf_status s = stage_query(bufs[i], q[i], &qs[i], st);
+    sf_status s = stage_query(bufs[i], q[i], &qs[i], st, ap);
     if (s != SF_OK) return fail(bufs[0], s, bufs[i]->err);
   }
-  return enqueue_attend(bufs, n, block, qs, out, scale, st);
+  return enqueue_attend(bufs, n, block, qs, out, scale, st, ap);
+}
+
+}  // namespace
+
+extern "C" {
+
+sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q, void* const* out,
+                    float scale, void* hip_stream) {
+  return attend_impl(bufs, n, block, q, out, scale, hip_stream, false);
+}
+
+sf_status sf_attend_static_scratch(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
+                                   void* const* out, float scale, void* hip_stream) {
+  return attend_impl(bufs, n, block, q, out, scale, hip_stream, true);
 }
 
 sf_status sf_step(sf_buffer* buf, int32_t block, int64_t t, const void* q, const void* k, const void* v, void* out,

@@ -240,6 +240,24 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
 sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
                     void* const* out, float scale, void* hip_stream);
 
+/* Allocation-free form of sf_attend, for callers that cannot allocate device memory or hand
+ * the library a workspace while they run: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks, kernels and results as sf_attend,
+ * but the read's scratch (the partial results of reads split across workgroups, and the
+ * turned query of a session under a rope mode) lives in a library-owned static device array
+ * of SF_STATIC_SCRATCH_BYTES instead of the sessions' memory; each GPU the library runs on
+ * holds its own copy until the process ends.  The call allocates nothing: the array's device
+ * address is looked up (hipGetSymbolAddress) on the first call on each device, with that
+ * device current.  A read whose scratch does not fit (the whole batch's, laid out one session
+ * after another) returns SF_E_UNSUPPORTED and enqueues nothing; a served read (16 heads of 64,
+ * 1,104 query rows, 6,528 keys) takes about 19.5 MB.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream are safe.  Nothing in the array needs to
+ * start at zero: each call writes every slot it reads. */
+#define SF_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+sf_status sf_attend_static_scratch(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
+                                   void* const* out, float scale, void* hip_stream);
+
 /* [files], [credits] The recency bias of a session configured with recency_bias = 1.
  * table: device pointer to [n_heads][w+1] fp32 (4-byte aligned, read by this call's launch
  * only; NULL allowed on a dry-run handle).  Entry [h][a] is added, in natural-log units, to
