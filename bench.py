@@ -437,6 +437,26 @@ def batched_leg(sf, sf_inputs, torch, steps, warmup=2):
     }
 
 
+def lds_copy_calibration(sf, torch, nbytes=64 << 20, reps=10):
+    """A copy of known size through LDS with the attention kernels' buffer-to-LDS transfer
+    (sf_debug_lds_copy): the reference the counter runs scale FETCH_SIZE by on that path."""
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sf.sf_debug_lds_copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    if not torch.equal(src, dst):
+        raise RuntimeError("sf_debug_lds_copy: copy differs from its source")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sf.sf_debug_lds_copy(dst, src, nbytes)
+    e1.record()
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"kernel": "lds_copy_kernel", "bytes_read": nbytes, "bytes_written": nbytes, "launches": reps + 1,
+            "avg_us": round(us, 3), "gbps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -580,6 +600,7 @@ def main():
         result["batched_leg"] = batched_leg(sf, sf_inputs, torch, args.steps)
     if not args.no_long_leg:
         result["long_leg"] = long_leg(sf, sf_inputs, torch, args.long_steps)
+    result["lds_copy_calibration"] = lds_copy_calibration(sf, torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, sink_gap)
     print(json.dumps(result), flush=True)

@@ -12,14 +12,17 @@
 // are floor(keys/64) full 64-key tiles plus, when keys is not a multiple of 64,
 // a tail of fewer than 64 keys.
 //   attn_sk_kernel: the full tiles of all units of the launch, in order, are cut
-//     into G equal contiguous ranges, one per persistent workgroup (G = number of
-//     CUs, one 8-wave workgroup per CU).  Consecutive ranges share a head, and the
-//     grid is remapped so each XCD (the hardware deals workgroups round robin over
-//     the 8 XCDs) owns a contiguous eighth: a head's K/V stays in one XCD's L2.
-//     The part of a unit inside one workgroup's range is a "piece"; a piece that is
-//     the whole unit (and the unit has no tail) writes the output, otherwise it
-//     writes an unnormalised partial (O, reference max, row sum) to the session's
-//     scratch;
+//     into G contiguous ranges, one per persistent workgroup (G = two 4-wave
+//     workgroups per CU).  The cut is made in cost units: a unit costs its tiles
+//     plus a fixed charge for its piece overhead (prologue and stream merge, about
+//     five tiles' worth), so a range that crosses into another unit holds fewer
+//     tiles and every workgroup finishes at about the same time.  Consecutive
+//     ranges share a head, and the grid is remapped so each XCD (the hardware deals
+//     workgroups round robin over the 8 XCDs) owns a contiguous eighth: a head's K/V
+//     stays in one XCD's L2.  The part of a unit inside one workgroup's range is a
+//     "piece"; a piece that is the whole unit (and the unit has no tail) writes the
+//     output, otherwise it writes an unnormalised partial (O, reference max, row
+//     sum) to the session's scratch;
 //   attn_tail_kernel: one workgroup per unit with a tail writes the tail's
 //     partial to the unit's last scratch slot;
 //   combine_sk_kernel: merges the partials of every unit that has more than one.
@@ -27,12 +30,18 @@
 // record's keys from the caller's K/V (segment slot kRecSlot, after the buffer's
 // keys) and combine_sk_kernel copies the record into the buffer.
 //
-// Inside a workgroup of attn_sk_kernel.  Eight waves = four key streams x two
-// waves; the piece's tiles are cut into four contiguous quarters, one per
-// stream.  The two waves of a stream hold 64 query rows each (two 32-row MFMA
-// blocks), so every K/V operand read from LDS feeds two MFMAs.  K and V tiles go
-// from global memory straight into LDS (global_load_lds_dwordx4, no staging
-// VGPRs), double buffered.
+// Inside a workgroup of attn_sk_kernel.  Four waves = two key streams x two waves;
+// the piece's tiles are cut into two contiguous halves, one per stream.  The two
+// waves of a stream hold 64 query rows each (two 32-row MFMA blocks), so every K/V
+// operand read from LDS feeds two MFMAs.  K and V tiles go from global memory
+// straight into LDS (buffer_load_dwordx4 ... lds: a scalar tile offset plus a lane
+// offset fixed for the piece, no staging VGPRs and no VALU address arithmetic),
+// double buffered.  Two such workgroups share a CU (256 VGPRs per wave, 2 waves per
+// SIMD): one's prologue and merge overlap the other's main loop.  The instruction
+// arbiter favours the wave dispatched first, which would leave the later workgroup
+// of a CU running alone at the end of the launch; each wave therefore sets its
+// priority from its workgroup's progress (3 in the first quarter of its range down
+// to 0 in the last), so the workgroup that is behind wins the arbiter.
 //
 // Softmax with a fixed reference.  Each stream takes one reference per query,
 // the max of the scores of its first 32 keys, and keeps it: p = exp2(s*c - mref) may
@@ -66,30 +75,50 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int D = 64;
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStreams = 4;
+constexpr int kStreams = 2;
 constexpr int BN = kSkKeys;                           // 64 keys per tile
 constexpr int ROW = 2 * D;                            // bytes per K/V row
 constexpr int TILE = BN * ROW;                        // 8 KB
 constexpr int STAGE = 2 * TILE;                       // K tile then V tile
-constexpr int STAGE_ALL = kStreams * STAGE;           // one stage of every stream (64 KB)
+constexpr int STAGE_ALL = kStreams * STAGE;           // one stage of every stream (32 KB)
 constexpr int DMA_ROWS = 8;                           // rows one wave-wide 1 KB transfer covers
 constexpr int DMA_PER_WAVE = BN / DMA_ROWS / 2;       // transfers per wave per tensor per tile (4)
 constexpr float kOverflowSum = 0x1p40f;               // a lane quarter sum above this asks for exact maxima
-// Stream merge buffer: 3 streams x 2 waves x 64 lanes x (64 O + 2 m + 2 l) floats,
-// slots 0-2 in stage array a, 3-5 in stage array b.
+// Stream merge buffer: stream 1's 2 waves x 64 lanes x (64 O + 2 m + 2 l) floats, the
+// slot of wave hw in stage array a (hw = 0) or b (hw = 1).
 constexpr int MERGE_FLOATS = 68;
 constexpr int MERGE_SLOT = 64 * MERGE_FLOATS * 4;
-static_assert(3 * MERGE_SLOT <= STAGE_ALL, "three merge slots fit in one stage array");
+static_assert(MERGE_SLOT <= STAGE_ALL, "a merge slot fits in one stage array");
 static_assert(BN == 64, "a tile is two 32-key MFMA blocks");
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
-// Workgroup holding iteration i when N iterations are cut into G ranges.
-__device__ __forceinline__ int wg_of_iter(long long i, int G, int N) {
-  return (int)(((i + 1) * G - 1) / N);
+// Issue priority from the workgroup's progress through its range: 3 in the first quarter
+// down to 0 in the last.  The workgroups sharing a CU then stay level with each other:
+// the one that is behind wins the instruction arbiter (which otherwise favours the wave
+// dispatched first), so neither ends up running alone at the end of the launch.
+__device__ __forceinline__ void progress_priority(const int done, const int total) {
+  const int q = (4 * done) / total;
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// p as a wave-uniform value (scalar registers).
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
+// Raw buffer resource from p with no range limit (gfx9 family dword3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, -1, 0x00020000);
 }
 
 __device__ __forceinline__ int session_of_iter(const SkLaunch& a, int it) {
@@ -97,6 +126,34 @@ __device__ __forceinline__ int session_of_iter(const SkLaunch& a, int it) {
   for (int i = 1; i < a.n_sessions; ++i)
     if (a.s[i].it_begin <= it) si = i;
   return __builtin_amdgcn_readfirstlane(si);
+}
+
+// Ranges are cut in cost units (a unit costs piece_cost, then one per tile), so a
+// workgroup whose range crosses into another unit gets fewer tiles.  pos(C): the
+// iteration at cost C (the piece_cost of a unit maps to its first tile).
+__device__ __forceinline__ int range_start(const SkLaunch& a, const int w) {
+  if (w >= a.n_wg) return a.n_iters;
+  const long long C = (long long)w * a.total_cost / a.n_wg;
+  int si = 0;
+  for (int i = 0; i < a.n_sessions; ++i)
+    if (a.s[i].ntiles > 0 && a.s[i].cost_begin <= C) si = i;
+  si = __builtin_amdgcn_readfirstlane(si);
+  const SkSession& S = a.s[si];
+  const long long per = S.ntiles + a.piece_cost;
+  const long long r0 = C - S.cost_begin;
+  const long long u = r0 / per;
+  const long long r = r0 - u * per - a.piece_cost;
+  return (int)(S.it_begin + u * S.ntiles + (r > 0 ? r : 0));
+}
+
+// Workgroup holding iteration i: the last w whose range starts at or before it.
+__device__ __forceinline__ int wg_of_iter(const SkLaunch& a, const int i) {
+  const SkSession& S = a.s[session_of_iter(a, i)];
+  const int local = i - S.it_begin;
+  const int u = local / S.ntiles;
+  const long long X = (long long)S.cost_begin + (long long)u * (S.ntiles + a.piece_cost) + a.piece_cost +
+                      (local - u * S.ntiles);
+  return (int)(((X + 1) * a.n_wg - 1) / a.total_cost);
 }
 
 // Session and unit of a unit index counted over the whole launch.
@@ -196,15 +253,15 @@ __device__ __forceinline__ int fresh_lane() {
 }
 
 template <bool REC>
-__global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
   __shared__ int redo[kWaves];
   const int G = a.n_wg;
   const int N = a.n_iters;
   const int w = (G & 7) == 0 ? (int)(wg_x() & 7u) * (G >> 3) + (int)(wg_x() >> 3) : (int)wg_x();
-  const int it_lo = __builtin_amdgcn_readfirstlane((int)((long long)w * N / G));
-  const int it_hi = __builtin_amdgcn_readfirstlane((int)((long long)(w + 1) * N / G));
+  const int it_lo = __builtin_amdgcn_readfirstlane(range_start(a, w));
+  const int it_hi = __builtin_amdgcn_readfirstlane(range_start(a, w + 1));
   const int H = a.n_heads;
   const float c = a.scale_log2;
 
@@ -274,10 +331,14 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
     seg_tables<REC>(S, seg_row, seg_key);
 
-    const char* __restrict__ kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
-    const char* __restrict__ vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
-    const char* __restrict__ krec = reinterpret_cast<const char*>(S.rec_k) + 2 * h * D;
-    const char* __restrict__ vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
+    // Buffer resources over the head's K and V (and the record's source): a transfer is a
+    // scalar tile offset plus a lane offset fixed for the piece, so it costs no VALU.
+    const char* __restrict__ kg = uniform_ptr(reinterpret_cast<const char*>(S.k) + 2 * h * D);
+    const char* __restrict__ vg = uniform_ptr(reinterpret_cast<const char*>(S.v) + 2 * h * D);
+    const char* __restrict__ krec = uniform_ptr(reinterpret_cast<const char*>(S.rec_k) + 2 * h * D);
+    const char* __restrict__ vrec = uniform_ptr(reinterpret_cast<const char*>(S.rec_v) + 2 * h * D);
+    const unsigned lane_k = (unsigned)(trow0 * row_bytes + kchunk * 16);
+    const unsigned lane_v = (unsigned)(trow0 * row_bytes + vchunk * 16);
 
     // Starts the transfer of this stream's tile TL into stage array ST (this wave's
     // half: rows [32*hw, 32*hw+32) of K and of V).  A tile inside one segment is a run
@@ -293,28 +354,32 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
         send = in ? (i + 1 < SF_MAX_SEGMENTS ? seg_key[i + 1 < SF_MAX_SEGMENTS ? i + 1 : i] : 0x7fffffff) : send;
         sidx = in ? i : sidx;
       }
+      srow = __builtin_amdgcn_readfirstlane(srow);  // uniform: tiles and segments are per workgroup
+      skey = __builtin_amdgcn_readfirstlane(skey);
+      send = __builtin_amdgcn_readfirstlane(send);
+      sidx = __builtin_amdgcn_readfirstlane(sidx);
       char* kdst = st + soff + (trow0 - drow) * ROW;
       char* vdst = kdst + TILE;
       constexpr int kStep = 2 * DMA_ROWS;  // rows between a wave's transfers
       if (kap0 + BN <= send) {
-        const char* kb = (REC && sidx == kRecSlot) ? krec : kg;
-        const char* vb = (REC && sidx == kRecSlot) ? vrec : vg;
-        const unsigned base = (unsigned)((srow + kap0 - skey + trow0) * row_bytes);
+        const bool rec = REC && sidx == kRecSlot;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(rec ? krec : kg);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(rec ? vrec : vg);
+        const unsigned base = (unsigned)((srow + kap0 - skey) * row_bytes);
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
-          const unsigned rb = base + (unsigned)(m * kStep * row_bytes);
-          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * kStep * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * kStep * ROW), 16, 0, 0);
+          const unsigned so = base + (unsigned)(m * kStep * row_bytes);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + m * kStep * ROW), 16, lane_k, so, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + m * kStep * ROW), 16, lane_v, so, 0, 0);
         }
       } else {
 #pragma unroll
         for (int m = 0; m < DMA_PER_WAVE; ++m) {
           int sg;
           const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kap0 + trow0 + m * kStep, sg) * row_bytes);
-          const char* kb = (REC && sg == kRecSlot) ? krec : kg;
-          const char* vb = (REC && sg == kRecSlot) ? vrec : vg;
-          __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(kdst + m * kStep * ROW), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(vdst + m * kStep * ROW), 16, 0, 0);
+          const bool rec = REC && sg == kRecSlot;
+          __builtin_amdgcn_global_load_lds((rec ? krec : kg) + rb + kchunk * 16, (lds_void*)(kdst + m * kStep * ROW), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((rec ? vrec : vg) + rb + vchunk * 16, (lds_void*)(vdst + m * kStep * ROW), 16, 0, 0);
         }
       }
     };
@@ -468,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       mref0 = fmaxf(mt0, xor32(mt0)) * c;
       mref1 = fmaxf(mt1, xor32(mt1)) * c;
       for (int i = 0; i < steps; i += 2) {
+        progress_priority(it - it_lo + kStreams * i, it_hi - it_lo);
         const int tl = s_lo + i;
         if (tl + 1 < s_hi) dma_tile(tl + 1, st_b);
         if (tl < s_hi && wave_on) SK_STEP_ABC(st_a);
@@ -496,10 +562,10 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
 
     if (it + (tile1 - tile0) < it_hi) load_q(it + (tile1 - tile0));  // the next piece's Q
 
-    // ---- merge the four streams (stream 0 collects), then write
+    // ---- merge the two streams (stream 0 collects), then write
     const int mlane = fresh_lane();
     auto merge_slot = [&](const int sl) -> float* {
-      return reinterpret_cast<float*>((sl < 3 ? st_a : st_b) + (sl % 3) * MERGE_SLOT) + mlane * MERGE_FLOATS;
+      return reinterpret_cast<float*>(sl == 0 ? st_a : st_b) + mlane * MERGE_FLOATS;
     };
     if (stream > 0 && wave_on) {
       float* dst = merge_slot((stream - 1) * 2 + hw);
@@ -516,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
     if (stream == 0 && wave_on) {
       float mx0 = mref0, mx1 = mref1;
 #pragma unroll
-      for (int s2 = 0; s2 < 3; ++s2) {
+      for (int s2 = 0; s2 < kStreams - 1; ++s2) {
         const float4 ml = *reinterpret_cast<const float4*>(merge_slot(s2 * 2 + hw) + 64);
         mx0 = fmaxf(mx0, ml.x);
         mx1 = fmaxf(mx1, ml.y);
@@ -529,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       o01 *= f01;
       o11 *= f01;
 #pragma unroll 1
-      for (int s2 = 0; s2 < 3; ++s2) {  // one stream at a time keeps the live set small
+      for (int s2 = 0; s2 < kStreams - 1; ++s2) {  // one stream at a time keeps the live set small
         const float* src = merge_slot(s2 * 2 + hw);
         const float4 ml = *reinterpret_cast<const float4*>(src + 64);
         const float f0 = __builtin_amdgcn_exp2f(ml.x - mx0);
@@ -552,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void attn_sk_kernel(const SkLaunch a) {
       const bool has_tail = (S.n_keys & (BN - 1)) != 0;
       const bool whole = tile0 == 0 && tile1 == nt && !has_tail;
       // piece slot of this unit: its k-th workgroup writes slot k
-      const int k = w - wg_of_iter((long long)S.it_begin + (long long)u * nt, G, N);
+      const int k = w - wg_of_iter(a, S.it_begin + u * nt);
       const int el32 = mlane & 31, eg = mlane >> 5;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -742,12 +808,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   int si, u;
   decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
-  const int G = a.n_wg, N = a.n_iters;
   const bool has_tail = (S.n_keys & (kSkKeys - 1)) != 0;
   int pieces = 0;
   if (S.ntiles > 0) {
-    const long long first = (long long)S.it_begin + (long long)u * S.ntiles;
-    pieces = wg_of_iter(first + S.ntiles - 1, G, N) - wg_of_iter(first, G, N) + 1;
+    const int first = S.it_begin + u * S.ntiles;
+    pieces = wg_of_iter(a, first + S.ntiles - 1) - wg_of_iter(a, first) + 1;
   }
   if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
   const int total = pieces + (has_tail ? 1 : 0);
@@ -807,8 +872,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
 }  // namespace
 
 int32_t sk_pieces_per_unit(int64_t capacity_rows) {
-  // pieces of a unit: at most ceil(tiles / kSkMinRange) + 1 (every workgroup has at
-  // least kSkMinRange tiles); one more slot for the tail
+  // pieces of a unit: at most ceil(tiles / kSkMinRange) + 1 (a workgroup range that
+  // starts inside a unit holds at least kSkMinRange of its tiles); one more slot for
+  // the tail
   const int64_t nt = capacity_rows / kSkKeys;
   return (int32_t)((nt + kSkMinRange - 1) / kSkMinRange + 2);
 }

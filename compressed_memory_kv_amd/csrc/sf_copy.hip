@@ -78,6 +78,34 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(char* __restrict__ mem,
 
 unsigned blocks_for(size_t n16) { return (unsigned)((n16 + kPerBlock - 1) / kPerBlock); }
 
+// Measurement aid: a copy through LDS with the transfer the head_dim-64 attention uses
+// for its K/V tiles (buffer_load_dwordx4 ... lds), so that hardware traffic counters can
+// be calibrated on that path.  Workgroup c moves the 16 KiB chunk c: each wave lands four
+// 1 KiB transfers in its own quarter of the LDS buffer, waits for them, reads its own
+// bytes back and stores them.
+constexpr int kLdsChunk = 16384;
+__global__ __launch_bounds__(kThreads) void lds_copy_kernel(char* __restrict__ dst, const char* __restrict__ src) {
+  __shared__ __attribute__((aligned(16))) char buf[kLdsChunk];
+  const size_t c = wg_x();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid_x() >> 6));  // uniform: scalar offsets
+  const int lane = (int)(tid_x() & 63);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + c * kLdsChunk, (short)0, kLdsChunk, 0x00020000);
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int off = wave * 4096 + m * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + off), 16, (unsigned)(lane * 16), (unsigned)off, 0,
+                                             0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's transfers have landed
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int off = wave * 4096 + m * 1024 + lane * 16;
+    *reinterpret_cast<u32x4*>(dst + c * kLdsChunk + off) = *reinterpret_cast<const u32x4*>(buf + off);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
@@ -118,6 +146,14 @@ hipError_t launch_evict(void* mem, int n_blocks, size_t block_stride, size_t v_o
   if (grid >= ((size_t)1 << 31)) return hipErrorInvalidValue;
   launch(evict_kernel, dim3((unsigned)grid), dim3(kThreads), stream, reinterpret_cast<char*>(mem),
                      block_stride, v_offset, src_off, dst_off, n16, per);
+  return hipGetLastError();
+}
+
+hipError_t launch_lds_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % kLdsChunk != 0 || bytes / kLdsChunk >= ((size_t)1 << 31)) return hipErrorInvalidValue;
+  launch(lds_copy_kernel, dim3((unsigned)(bytes / kLdsChunk)), dim3(kThreads), stream, reinterpret_cast<char*>(dst),
+         reinterpret_cast<const char*>(src));
   return hipGetLastError();
 }
 

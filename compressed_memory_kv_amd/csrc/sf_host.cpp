@@ -608,7 +608,8 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     a.n_sessions = cnt;
     a.n_heads = H;
     a.scale_log2 = scale_log2;
-    int64_t iters = 0, units_total = 0;
+    int64_t iters = 0, units_total = 0, cost = 0;
+    const int piece_cost = sf::kSkPieceCost;
     bool any_tail = false;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
@@ -642,23 +643,28 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       any_tail = any_tail || (sg.keys % sf::kSkKeys) != 0;
       const int64_t units = (int64_t)H * s.qtiles;
       s.it_begin = (int32_t)iters;
+      s.cost_begin = (int32_t)cost;
       iters += units * s.ntiles;
+      cost += s.ntiles > 0 ? units * (s.ntiles + piece_cost) : 0;
       units_total += units;
     }
-    if (iters >= ((int64_t)1 << 30) || units_total >= ((int64_t)1 << 28))
+    if (iters >= ((int64_t)1 << 30) || units_total >= ((int64_t)1 << 28) || cost >= ((int64_t)1 << 31))
       return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
-    int64_t G = device_cu_count();
+    int64_t G = (int64_t)sf::kSkWgPerCu * device_cu_count();
     if (G > iters / sf::kSkMinRange) G = iters / sf::kSkMinRange;
     if (G < 1) G = 1;
     if (G >= 8) G -= G % 8;
     a.n_wg = (int32_t)G;
     a.n_iters = (int32_t)iters;
-    // Partial-result slots per unit: every workgroup range holds at least floor(N / G)
-    // tiles, so a unit of ntiles tiles meets at most ceil(ntiles / that) + 1 ranges; one
-    // more slot for the tail.  G <= N / kSkMinRange makes floor(N / G) >= kSkMinRange (or
-    // G = 1 and one range holds every tile), so this never exceeds the capacity bound the
-    // session's own scratch region is sized for.
-    const int64_t per_wg = iters / G > 0 ? iters / G : 1;
+    a.piece_cost = piece_cost;
+    a.total_cost = (int32_t)cost;
+    // Partial-result slots per unit: every workgroup range spans at least floor(T / G)
+    // cost units, and one that starts past a unit's first tile holds that many tiles of
+    // it, so a unit of ntiles tiles meets at most ceil(ntiles / floor(T / G)) + 1 ranges;
+    // one more slot for the tail.  G <= N / kSkMinRange and T >= N make floor(T / G) >=
+    // kSkMinRange (or G = 1 and one range holds every tile), so this never exceeds the
+    // capacity bound the session's own scratch region is sized for.
+    const int64_t per_wg = cost / G > 0 ? cost / G : 1;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       sf::SkSession& s = a.s[i];
@@ -1353,6 +1359,19 @@ sf_status sf_kernel_times_read(sf_buffer* buf, sf_kernel_times* out) {
 sf_status sf_debug_fail_next_launch(sf_buffer* buf) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   buf->fail_next = true;
+  return SF_OK;
+}
+
+sf_status sf_debug_lds_copy(void* dst, const void* src, size_t bytes, void* hip_stream) {
+  if (bytes == 0) return SF_OK;
+  if (!dst || !src) return fail(nullptr, SF_E_ARG, "sf_debug_lds_copy: NULL pointer");
+  if (!aligned16(dst) || !aligned16(src)) return fail(nullptr, SF_E_ARG, "sf_debug_lds_copy: pointers must be 16-byte aligned");
+  if (bytes % 16384 != 0) return fail(nullptr, SF_E_ARG, "sf_debug_lds_copy: bytes must be a multiple of 16384");
+  const char* d = static_cast<const char*>(dst);
+  const char* s = static_cast<const char*>(src);
+  if (d < s + bytes && s < d + bytes) return fail(nullptr, SF_E_ARG, "sf_debug_lds_copy: regions overlap");
+  hipError_t e = sf::launch_lds_copy(dst, src, bytes, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(nullptr, SF_E_HIP, std::string("sf_debug_lds_copy: ") + hipGetErrorString(e));
   return SF_OK;
 }
 

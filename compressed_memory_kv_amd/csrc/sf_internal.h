@@ -76,14 +76,16 @@ struct AttnLaunch {
 
 // ---- persistent stream-K attention (bf16, head_dim 64) ----------------------
 // The launch's work is the flattened sequence of (session, head, 128-row query
-// tile, full 64-key tile) iterations; workgroup w takes iterations
-// [w*N/G, (w+1)*N/G).  A query tile that spans several workgroups leaves one
+// tile, full 64-key tile) iterations; workgroup w takes the iterations between
+// costs floor(w*T/G) and floor((w+1)*T/G) (see SkLaunch::piece_cost).  A query tile that spans several workgroups leaves one
 // partial result per workgroup ("piece") in its session's scratch; keys past the
 // last full tile (the tail) leave one more, from the tail kernel, in the unit's
 // last slot; the combine kernel merges them.
 constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
-constexpr int kSkMinRange = 8;      // fewest tiles a workgroup is given
+constexpr int kSkMinRange = 8;      // fewest cost units a workgroup is given
+constexpr int kSkWgPerCu = 2;       // persistent workgroups per CU
+constexpr int kSkPieceCost = 5;     // a piece's fixed overhead, in tiles
 constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
@@ -107,7 +109,8 @@ struct SkSession {
   int32_t ntiles;       // full key tiles: n_keys / kSkKeys
   int32_t ppu;          // piece slots per unit in the scratch
   int32_t it_begin;     // first iteration of this session in the launch
-  int32_t pad[3];
+  int32_t cost_begin;   // first cost unit of this session (see SkLaunch::piece_cost)
+  int32_t pad[2];
   int32_t seg_begin[SF_MAX_SEGMENTS];
   int32_t seg_len[SF_MAX_SEGMENTS];
 };
@@ -117,11 +120,16 @@ struct SkLaunch {
   int32_t n_wg;         // G
   int32_t n_iters;      // N
   float scale_log2;
-  int32_t pad[3];
+  // Workgroup ranges are cut in cost units: a unit of ntiles full tiles costs
+  // ntiles + piece_cost (its piece overhead, in tiles), a unit without full tiles 0;
+  // total_cost = T.  Workgroup w starts at the iteration of cost floor(w*T/G).
+  int32_t piece_cost;
+  int32_t total_cost;
+  int32_t pad[1];
   SkSession s[kMaxLaunchSessions];
 };
-// Piece slots per unit a session of capacity C needs (bounded because every
-// workgroup gets at least kSkMinRange tiles).
+// Piece slots per unit a session of capacity C needs (bounded because a workgroup
+// range that starts inside a unit holds at least kSkMinRange of its tiles).
 int32_t sk_pieces_per_unit(int64_t capacity_rows);
 size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows);
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream);
@@ -142,6 +150,7 @@ hipError_t launch_copy_rows(void* dst_k, void* dst_v, const void* src_k, const v
                             size_t bytes, hipStream_t stream);
 // Copies `bytes` from src_off to dst_off inside K and V of every block:
 // block b's K starts at mem + b*block_stride, its V at that + v_offset.
+hipError_t launch_lds_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_evict(void* mem, int n_blocks, size_t block_stride, size_t v_offset,
                         size_t src_off, size_t dst_off, size_t bytes, hipStream_t stream);
 // Rotary tables: the first n_planes (dims 2i, 2i+1) planes of a head turn by the angle

@@ -250,7 +250,7 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
  * address is looked up (hipGetSymbolAddress) on the first call on each device, with that
  * device current.  A read whose scratch does not fit (the whole batch's, laid out one session
  * after another) returns SF_E_UNSUPPORTED and enqueues nothing; a served read (16 heads of 64,
- * 1,104 query rows, 6,528 keys) takes about 19.5 MB.  Every call on a GPU shares that GPU's
+ * 1,104 query rows, 6,528 keys) takes about 29.2 MB.  Every call on a GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, other threads) race and give
  * undefined results; calls ordered on one stream are safe.  Nothing in the array needs to
  * start at zero: each call writes every slot it reads. */
@@ -320,6 +320,14 @@ typedef struct sf_kernel_times {
 /* on != 0 enables, 0 disables (pending events are dropped).  Dry-run handles: SF_E_STATE. */
 sf_status sf_profile_enable(sf_buffer* buf, int32_t on);
 sf_status sf_kernel_times_read(sf_buffer* buf, sf_kernel_times* out);
+
+/* Measurement aid, not part of the method: copies `bytes` from src to dst (device pointers,
+ * 16-byte aligned, bytes a multiple of 16384, regions not overlapping) through LDS with the
+ * buffer-to-LDS transfer the head_dim-64 attention uses for its K/V tiles, on hip_stream
+ * (NULL: the default stream), so that hardware traffic counters (FETCH_SIZE) can be
+ * calibrated on that path against a copy of known size.  SF_E_ARG on a bad pointer or
+ * size, SF_E_HIP on a launch failure; enqueues nothing on error. */
+sf_status sf_debug_lds_copy(void* dst, const void* src, size_t bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -453,3 +453,13 @@ def test_recency_bias_sizes_and_rules():
     with pytest.raises(sf.SfError) as ei:
         sf.sf_set_recency_bias(0, None)
     assert ei.value.status == sf.SF_E_ARG
+
+
+def test_lds_copy_argument_checks():
+    """The calibration copy checks its arguments before any launch (no GPU needed)."""
+    sf.sf_debug_lds_copy(0x100000, 0x200000, 0)  # nothing to copy: no launch
+    for dst, src, n in ((0, 0x200000, 16384), (0x100008, 0x200000, 16384), (0x100000, 0x200000, 16000),
+                        (0x100000, 0x102000, 16384)):
+        with pytest.raises(sf.SfError) as ei:
+            sf.sf_debug_lds_copy(dst, src, n)
+        assert ei.value.status == sf.SF_E_ARG

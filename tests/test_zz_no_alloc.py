@@ -71,7 +71,7 @@ SMALL128 = dict(SMALL, head_dim=128, seed=22)
 
 @needs_gpu
 def test_static_scratch_stream_k_two_calls():
-    """Served shape at frame 31 (6,528 keys, ~19.5 MB of partials), then a smaller session
+    """Served shape at frame 31 (6,528 keys, ~29.2 MB of partials), then a smaller session
     (2,600 keys, a 40-key tail) at a caller scale."""
     big, qb = replayed(SERVED, 31)
     both_reads([big], [qb], "served t=31")
