@@ -41,9 +41,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libsf.so")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compiles every source and links libsf.so; returns its path.  Always recompiles."""
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, file_flags: dict | None = None,
+          link_flags: list | None = None) -> str:
+    """Compiles every source and links libsf.so (or `out`); returns its path.  Always
+    recompiles.  file_flags adds per-source flags, link_flags flags of the link step."""
     cc = hipcc()
+    extra = file_flags or {}
     tmp = tempfile.mkdtemp(prefix="sfbuild_")
     try:
         procs = []
@@ -52,22 +55,24 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"]
-            cmd = [cc, *COMMON_FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON_FLAGS, *FILE_FLAGS.get(src, []), *extra.get(src, []), *lang, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
             if len(procs) >= jobs:
                 _drain(procs)
         _drain(procs)
-        out_tmp = LIB + ".tmp"
-        cmd = [cc, *COMMON_FLAGS, "-shared", *objs, "-o", out_tmp]
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        out_tmp = out + ".tmp"
+        cmd = [cc, *COMMON_FLAGS, "-shared", *objs, *(link_flags or []), "-o", out_tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
-        os.replace(out_tmp, LIB)
-        return LIB
+        os.replace(out_tmp, out)
+        return out
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
 

@@ -1309,7 +1309,11 @@ sf_status sf_plan(const sf_config* cfg, int64_t t, sf_view* view) {
 }
 
 const char* sf_status_str(sf_status s) {
-  switch (s) {
+  // C callers may pass any int: read the argument's bytes as one (a C++ load of an enum
+  // value outside the enumerators' range is undefined).
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SF_OK: return "SF_OK";
     case SF_E_ARG: return "SF_E_ARG";
     case SF_E_ORDER: return "SF_E_ORDER";
