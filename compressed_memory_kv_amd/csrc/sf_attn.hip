@@ -12,9 +12,11 @@
 //
 // bf16 kernel (attn_bf16_kernel<D>, D = head_dim 64 or 128)
 //   workgroup = 4 waves = 128 query rows of one head; wave = 32 query rows.
-//   Keys go in tiles of 64 rows; K and V tiles are staged in LDS (double
-//   buffered, XOR-swizzled 16/32-byte chunks so MFMA operand reads are
-//   bank-conflict free).  Per tile and wave:
+//   Keys go in tiles of 64 rows; K and V tiles go from global memory straight
+//   into LDS (buffer_load_dwordx4 ... lds: a scalar tile offset plus a lane
+//   offset fixed for the unit, no staging registers), double buffered in two
+//   LDS arrays, as XOR-swizzled 16-byte chunks so MFMA operand reads are
+//   bank-conflict free.  Per tile and wave:
 //     S^T (64 keys x 32 queries) = K_tile . Q^T   on v_mfma_f32_32x32x16_bf16
 //       (A = K rows from LDS, B = Q held in VGPRs for the whole loop), so each
 //       lane owns one query and 32 of its scores: the row max is in-lane plus
@@ -22,8 +24,8 @@
 //     online softmax in fp32 with exp2 (scale*log2e folded into one FMA); the
 //       reference max is raised only when a tile's max exceeds it by more than
 //       2^8, so rescaling the accumulator is rare;
-//     P rounded to bf16 (round to nearest even) and its row sum taken from
-//       those rounded values (v_dot2_f32_bf16 against ones);
+//     P rounded to bf16 (round to nearest even); the row sum adds the fp32
+//       values;
 //     O^T (D x 32 queries) += V^T . P^T  on the same MFMA; the V^T operand is
 //       read from the row-major V tile with ds_read_b64_tr_b16 (each 16-lane
 //       group turns four 8-byte row pieces into four consecutive keys per
@@ -52,7 +54,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -153,6 +154,21 @@ struct Tile {
   static __device__ __forceinline__ int vsw(int r) { return D == 64 ? 2 * (r & 3) : 4 * (r & 3); }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// p as a wave-uniform value (scalar registers).
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
+// Raw buffer resource from p with no range limit (gfx9 family dword3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, -1, 0x00020000);
+}
+
 // Probability sums above this make the tile recompute against its true max: every
 // p stays <= 2^15 in the accumulators, and p of the first tile (reference -inf) is inf.
 constexpr float kSumLimit = 32768.0f;
@@ -161,13 +177,15 @@ template <int D, bool BIAS>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a) {
   using T = Tile<D>;
   constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int PER = BN * CH / kThreads;    // chunks per thread per tensor per tile
   constexpr int KSTEPS = D / 16;             // MFMA k-steps over head_dim
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
-  static_assert(PER * kThreads == BN * CH, "tile loads divide evenly");
   static_assert(BN <= kThreads, "one thread stages each key's bias");
-  constexpr int BIAS_OFF = 2 * T::STAGE;    // two stages of BN fp32 biases follow the K/V stages
-  __shared__ __attribute__((aligned(16))) char sm[2 * T::STAGE + (BIAS ? 2 * BN * 4 : 0)];
+  // Two stages, each in an array of its own: the compiler then knows that transfers into
+  // one stage never alias the operand reads of the other (one array would make it wait for
+  // every transfer in flight before each LDS read).
+  __shared__ __attribute__((aligned(16))) char st_a[T::STAGE + (BIAS ? BN * 4 : 0)];
+  __shared__ __attribute__((aligned(16))) char st_b[T::STAGE + (BIAS ? BN * 4 : 0)];
+  constexpr int BIAS_OFF = T::STAGE;        // the tile's BN fp32 biases follow its K/V
 
   const int unit = unit_of_block(a.total_units);
   if (unit >= a.total_units) return;
@@ -201,19 +219,23 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
   }
 
-  // Per-thread tile-load geometry (loop invariant).  Chunk p of this thread is row
-  // tid/CH + p*RSTEP, chunk tid%CH; rows p*RSTEP apart share their swizzles (both
-  // depend on row & 15 at most), so every chunk's global and LDS offsets are those
-  // of chunk 0 plus a constant.
-  constexpr int RSTEP = kThreads / CH;
-  static_assert(RSTEP % 16 == 0, "chunks of one thread share their swizzle");
-  const char* __restrict__ kg = U.k + 2 * U.h * D;
-  const char* __restrict__ vg = U.v + 2 * U.h * D;
-  const int prow = tid / CH;
-  const unsigned goff = (unsigned)(prow * row_bytes + (tid % CH) * 16);
-  const unsigned gstep = (unsigned)(RSTEP * row_bytes);
-  const int ksoff = prow * T::ROW + (((tid % CH) ^ T::ksw(prow)) << 4);
-  const int vsoff = T::KBYTES + prow * T::ROW + (((tid % CH) ^ T::vsw(prow)) << 4);
+  // K/V tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds, no
+  // staging registers).  One wave-wide transfer fills 1 KB = RPT rows of a stage, lane L
+  // landing at row L / CH, chunk position L % CH; lane L therefore fetches the logical
+  // chunk that belongs there (the swizzles are involutions).  Wave w takes the transfers
+  // starting at rows RPT*w + 4*RPT*m, which all have the same row phase modulo 16, so each
+  // lane fetches the same K chunk and the same V chunk in every transfer of the piece.
+  constexpr int RPT = 1024 / T::ROW;          // rows per transfer (4 at D = 128, 8 at D = 64)
+  constexpr int NTW = BN / RPT / kWaves;      // transfers per wave per tensor per tile
+  static_assert(NTW * RPT * kWaves == BN, "transfers divide the tile");
+  const char* __restrict__ kg = uniform_ptr(U.k + 2 * U.h * D);
+  const char* __restrict__ vg = uniform_ptr(U.v + 2 * U.h * D);
+  const int rl = lane / CH;                   // row of this lane within a transfer
+  const int r0w = RPT * wave;                 // first row of this wave's transfer 0
+  const int kchunk = (lane % CH) ^ T::ksw(r0w + rl);
+  const int vchunk = (lane % CH) ^ T::vsw(r0w + rl);
+  const unsigned lane_k = (unsigned)(rl * row_bytes + kchunk * 16);
+  const unsigned lane_v = (unsigned)(rl * row_bytes + vchunk * 16);
   // Per-lane LDS operand addresses (bytes within a stage).
   int kaddr[KSTEPS];
 #pragma unroll
@@ -226,46 +248,54 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     vaddr[db] = T::KBYTES + (4 * g + trow) * T::ROW + ((chunk ^ T::vsw(trow)) << 4) + 8 * (lane & 1);
   }
 
-  // Loads tile TILE into staging registers KR/VR.  A tile inside one segment is a
-  // run of rows: a scalar base plus the fixed per-thread offsets.  Otherwise each
-  // row is looked up; keys past the unit's range re-read its last key (finite
-  // data) and get score -inf.
-#define SF_LOAD_TILE(TILE, KR, VR, BR)                                                      \
-  {                                                                                         \
-    const int kap0_ = (TILE) * BN;                                                          \
-    if constexpr (BIAS) {                                                                   \
-      if (tid < BN) BR = brow ? brow[key_row(U, min(kap0_ + tid, key_hi - 1))] : 0.0f;      \
-    }                                                                                       \
-    int srow_ = U.seg_row[0], skey_ = U.seg_key[0], send_ = U.seg_key[1];                   \
-    _Pragma("unroll") for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {                           \
-      const bool in_ = kap0_ >= U.seg_key[i];                                               \
-      srow_ = in_ ? U.seg_row[i] : srow_;                                                   \
-      skey_ = in_ ? U.seg_key[i] : skey_;                                                   \
-      send_ = in_ ? (i + 1 < SF_MAX_SEGMENTS ? U.seg_key[i + 1 < SF_MAX_SEGMENTS ? i + 1 : i] : 0x7fffffff) : send_; \
-    }                                                                                       \
-    if (kap0_ + BN <= min(send_, key_hi)) {                                                 \
-      const unsigned base_ = (unsigned)((srow_ + kap0_ - skey_) * row_bytes);               \
-      _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                     \
-        KR[p] = *reinterpret_cast<const u32x4*>(kg + base_ + p * gstep + goff);             \
-        VR[p] = *reinterpret_cast<const u32x4*>(vg + base_ + p * gstep + goff);             \
-      }                                                                                     \
-    } else {                                                                                \
-      _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                     \
-        const int kappa_ = min(kap0_ + prow + p * RSTEP, key_hi - 1);                       \
-        const unsigned off_ = (unsigned)(key_row(U, kappa_) * row_bytes) + (tid % CH) * 16; \
-        KR[p] = *reinterpret_cast<const u32x4*>(kg + off_);                                 \
-        VR[p] = *reinterpret_cast<const u32x4*>(vg + off_);                                 \
-      }                                                                                     \
-    }                                                                                       \
-  }
-#define SF_STORE_TILE(STAGE_BYTES, KR, VR, BR)                                              \
-  _Pragma("unroll") for (int p = 0; p < PER; ++p) {                                         \
-    *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + ksoff + p * RSTEP * T::ROW) = KR[p];     \
-    *reinterpret_cast<u32x4*>(sm + (STAGE_BYTES) + vsoff + p * RSTEP * T::ROW) = VR[p];     \
-  }                                                                                         \
-  if constexpr (BIAS) {                                                                     \
-    if (tid < BN) reinterpret_cast<float*>(sm + BIAS_OFF + ((STAGE_BYTES) / T::STAGE) * BN * 4)[tid] = BR; \
-  }
+  // Starts the transfers of tile TILE into stage ST (this wave's rows of K and V).  A tile
+  // inside one segment is a run of rows: a scalar offset plus the fixed lane offsets.
+  // Otherwise each row is looked up; keys past the unit's range re-read its last key
+  // (finite data) and get score -inf.  The bias of the tile's keys (BIAS) goes through a
+  // register: loaded here into BR, stored by store_bias after the stage's compute.
+  auto dma_tile = [&](const int tile, char* st, float& br) {
+    const int kap0 = tile * BN;
+    if constexpr (BIAS) {
+      if (tid < BN) br = brow ? brow[key_row(U, min(kap0 + tid, key_hi - 1))] : 0.0f;
+    }
+    int srow = U.seg_row[0], skey = U.seg_key[0], send = U.seg_key[1];
+#pragma unroll
+    for (int i = 1; i < SF_MAX_SEGMENTS; ++i) {
+      const bool in = kap0 >= U.seg_key[i];
+      srow = in ? U.seg_row[i] : srow;
+      skey = in ? U.seg_key[i] : skey;
+      send = in ? (i + 1 < SF_MAX_SEGMENTS ? U.seg_key[i + 1 < SF_MAX_SEGMENTS ? i + 1 : i] : 0x7fffffff) : send;
+    }
+    srow = __builtin_amdgcn_readfirstlane(srow);
+    skey = __builtin_amdgcn_readfirstlane(skey);
+    send = __builtin_amdgcn_readfirstlane(send);
+    if (kap0 + BN <= min(send, key_hi)) {
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg);
+      const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg);
+      const unsigned base = (unsigned)((srow + kap0 - skey + r0w) * row_bytes);
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const unsigned so = base + (unsigned)(m * 4 * RPT * row_bytes);
+        char* dk = st + (r0w + m * 4 * RPT) * T::ROW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dk, 16, lane_k, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dk + T::KBYTES), 16, lane_v, so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const int kappa = min(kap0 + r0w + m * 4 * RPT + rl, key_hi - 1);
+        const unsigned rb = (unsigned)(key_row(U, kappa) * row_bytes);
+        char* dk = st + (r0w + m * 4 * RPT) * T::ROW;
+        __builtin_amdgcn_global_load_lds(kg + rb + kchunk * 16, (lds_void*)dk, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vg + rb + vchunk * 16, (lds_void*)(dk + T::KBYTES), 16, 0, 0);
+      }
+    }
+  };
+  auto store_bias = [&](char* st, const float br) {
+    if constexpr (BIAS) {
+      if (tid < BN) reinterpret_cast<float*>(st + BIAS_OFF)[tid] = br;
+    }
+  };
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -274,11 +304,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mref = -INFINITY;  // reference max, log2 units
   float lsum = 0.0f;       // this lane's share of the row sum
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One tile of work on the stage at byte offset ST.
-  auto compute_tile = [&](const int tile, const int ST) {
-    const char* st = sm + ST;
+  auto compute_tile = [&](const int tile, const char* st) {
     // ---- S^T = K . Q^T : two 32-key blocks
     f32x16 s0, s1;
 #pragma unroll
@@ -302,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     // ---- recency bias: scores to log2 units with each key's bias added (register r of
     // block b holds key 32b + 8(r/4) + 4g + r%4); from here on the scale is 1.
     if constexpr (BIAS) {
-      const float* bs = reinterpret_cast<const float*>(sm + BIAS_OFF + (ST / T::STAGE) * BN * 4);
+      const float* bs = reinterpret_cast<const float*>(st + BIAS_OFF);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4 b0 = *reinterpret_cast<const float4*>(bs + 8 * q4 + 4 * g);
@@ -322,21 +350,17 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     bf16x8 pb[4];
     float ts;
     auto probs = [&]() {
+      float part[4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        pb[0][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cs, -mref));
-        pb[1][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 + r], cs, -mref));
-        pb[2][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cs, -mref));
-        pb[3][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 + r], cs, -mref));
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& sj = j < 2 ? s0 : s1;
+        float e[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[8 * (j & 1) + r], cs, -mref));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pb[j][r] = (__bf16)e[r];
+        part[j] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {pb[j][2 * e], pb[j][2 * e + 1]};
-          part[j] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part[j], false);
-        }
       ts = (part[0] + part[1]) + (part[2] + part[3]);
     };
     probs();
@@ -373,29 +397,24 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
     }
   };
 
-  // Pipeline: tile i is computed from stage i&1 while tile i+2 is in flight in one
-  // register set and tile i+1 (the other set) is stored to stage (i+1)&1 after it.
-  u32x4 kra[PER], vra[PER], krb[PER], vrb[PER];
-  float bra = 0.0f, brb = 0.0f;  // this thread's key bias of each set (BIAS only)
-  SF_LOAD_TILE(t0, kra, vra, bra)
-  if (t0 + 1 < t1) SF_LOAD_TILE(t0 + 1, krb, vrb, brb)
-  SF_STORE_TILE(0, kra, vra, bra)
+  // Pipeline: tile i is computed from stage i&1 while tile i+1 lands in the other stage;
+  // the barrier after each compute waits for this wave's transfers (and the stage's bias
+  // store) and for every wave to be done with the stage the next step refills.
+  float bra = 0.0f, brb = 0.0f;  // this thread's key bias of each stage (BIAS only)
+  dma_tile(t0, st_a, bra);
+  store_bias(st_a, bra);
   __syncthreads();
   for (int tile = t0; tile < t1; tile += 2) {
-    // even step: compute stage 0, refill set a with tile+2, store set b (tile+1) to stage 1
-    if (tile + 2 < t1) SF_LOAD_TILE(tile + 2, kra, vra, bra)
-    if (wave_on) compute_tile(tile, 0);
-    if (tile + 1 < t1) SF_STORE_TILE(T::STAGE, krb, vrb, brb)
+    if (tile + 1 < t1) dma_tile(tile + 1, st_b, brb);
+    if (wave_on) compute_tile(tile, st_a);
+    if (tile + 1 < t1) store_bias(st_b, brb);
     __syncthreads();
     if (tile + 1 >= t1) break;
-    // odd step: compute stage 1, refill set b with tile+3, store set a (tile+2) to stage 0
-    if (tile + 3 < t1) SF_LOAD_TILE(tile + 3, krb, vrb, brb)
-    if (wave_on) compute_tile(tile + 1, T::STAGE);
-    if (tile + 2 < t1) SF_STORE_TILE(0, kra, vra, bra)
+    if (tile + 2 < t1) dma_tile(tile + 2, st_a, bra);
+    if (wave_on) compute_tile(tile + 1, st_b);
+    if (tile + 2 < t1) store_bias(st_a, bra);
     __syncthreads();
   }
-#undef SF_LOAD_TILE
-#undef SF_STORE_TILE
 
   if (!wave_on) return;
   const float ltot = lsum + xor32(lsum);
