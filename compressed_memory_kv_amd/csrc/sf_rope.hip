@@ -86,9 +86,14 @@ __device__ __forceinline__ void turn_planes(unsigned w[4], int p0, bool summary,
 
 // Sink: NP temporal planes of one head start its row: NP * (bf16 ? 4 : 8) bytes, 16-byte
 // aligned (a head row is 128 or 256 bytes), cut into 16-byte chunks (the last may be 8
-// bytes).  One thread per chunk of a (block, Z0 row, head); grid row = block.  Rows from
+// bytes).  Chunks of (block, Z0 row, head) are numbered per block; a thread takes
+// kSinkPer of them, kRopeThreads apart (each load instruction of a wave covers
+// consecutive chunks), and issues all its loads before the first store, so that many
+// bytes are in flight: the line size makes the memory system move whole 128-byte head
+// rows for the 48 (or 88) bytes the planes hold.  Grid row = block.  Rows from
 // `lvl_row0` on keep their two slowest planes (the level axis under the replace reading);
 // lvl_row0 >= rows turns every plane of every row.
+constexpr int kSinkPer = 4;
 template <bool BF16, int NP>
 __global__ __launch_bounds__(kRopeThreads) void sink_rotate_kernel(char* __restrict__ mem, size_t block_stride,
                                                                     int lvl_row0, int rows, int heads, int head_dim,
@@ -98,40 +103,49 @@ __global__ __launch_bounds__(kRopeThreads) void sink_rotate_kernel(char* __restr
   constexpr int NC = (BYTES + 15) / 16;                // chunks per head
   constexpr int PPC = 16 / EB;                         // planes per full chunk
   const unsigned per_block = (unsigned)rows * (unsigned)heads * NC;  // < 2^31 (checked at launch)
-  const unsigned idx = wg_x() * kRopeThreads + tid_x();
-  if (idx >= per_block) return;
-  const unsigned b = wg_y();                           // one grid row per block
-  const unsigned rh = idx / NC;                        // row * heads + head
-  const int ch = (int)(idx - rh * NC);
-  const bool keep_level = (int)(rh / (unsigned)heads) >= lvl_row0;
-  char* p = mem + (size_t)b * block_stride + (size_t)rh * head_dim * (BF16 ? 2 : 4) + 16 * ch;
-  const bool full = (ch + 1) * 16 <= BYTES;
-  unsigned w[4];
-  if (full) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
-  } else {                                             // the 8-byte tail chunk
-    const unsigned* q = reinterpret_cast<const unsigned*>(p);
-    w[0] = q[0];
-    w[1] = q[1];
-    w[2] = 0u;
-    w[3] = 0u;
+  const unsigned first = wg_x() * (kRopeThreads * kSinkPer) + tid_x();
+  char* base = mem + (size_t)wg_y() * block_stride;   // one grid row per block
+  unsigned w[kSinkPer][4];
+  char* p[kSinkPer];
+  int ch[kSinkPer];
+#pragma unroll
+  for (int k = 0; k < kSinkPer; ++k) {
+    const unsigned idx = first + k * kRopeThreads;
+    const unsigned rh = idx / NC;                      // row * heads + head
+    ch[k] = (int)(idx - rh * NC);
+    p[k] = base + (size_t)rh * head_dim * (BF16 ? 2 : 4) + 16 * ch[k];
+    w[k][0] = w[k][1] = w[k][2] = w[k][3] = 0u;
+    if (idx >= per_block) continue;
+    if ((ch[k] + 1) * 16 <= BYTES) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p[k]);
+      w[k][0] = v.x;
+      w[k][1] = v.y;
+      w[k][2] = v.z;
+      w[k][3] = v.w;
+    } else {                                           // the 8-byte tail chunk
+      const unsigned* q = reinterpret_cast<const unsigned*>(p[k]);
+      w[k][0] = q[0];
+      w[k][1] = q[1];
+    }
   }
-  turn_planes<BF16, NP>(w, ch * PPC, keep_level, kKeep, tab);
-  if (full) {
-    u32x4 v;
-    v.x = w[0];
-    v.y = w[1];
-    v.z = w[2];
-    v.w = w[3];
-    *reinterpret_cast<u32x4*>(p) = v;
-  } else {
-    unsigned* q = reinterpret_cast<unsigned*>(p);
-    q[0] = w[0];
-    q[1] = w[1];
+#pragma unroll
+  for (int k = 0; k < kSinkPer; ++k) {
+    const unsigned idx = first + k * kRopeThreads;
+    if (idx >= per_block) continue;
+    const bool keep_level = (int)(idx / NC / (unsigned)heads) >= lvl_row0;
+    turn_planes<BF16, NP>(w[k], ch[k] * PPC, keep_level, kKeep, tab);
+    if ((ch[k] + 1) * 16 <= BYTES) {
+      u32x4 v;
+      v.x = w[k][0];
+      v.y = w[k][1];
+      v.z = w[k][2];
+      v.w = w[k][3];
+      *reinterpret_cast<u32x4*>(p[k]) = v;
+    } else {
+      unsigned* q = reinterpret_cast<unsigned*>(p[k]);
+      q[0] = w[k][0];
+      q[1] = w[k][1];
+    }
   }
 }
 
@@ -183,7 +197,7 @@ hipError_t launch_sink_rotate(void* mem, int n_blocks, size_t block_stride, int 
   const long long n = (long long)rows * heads * ((tab.n_planes * eb + 15) / 16);  // threads per block
   if (n == 0 || n_blocks == 0) return hipSuccess;
   if (n >= (1LL << 31) || n_blocks > 65535) return hipErrorInvalidValue;
-  const long long grid = (n + kRopeThreads - 1) / kRopeThreads;
+  const long long grid = (n + kRopeThreads * kSinkPer - 1) / (kRopeThreads * kSinkPer);
   // the temporal band of the two head sizes: 12 planes at 64, 22 at 128
   char* m = static_cast<char*>(mem);
   const dim3 g((unsigned)grid, (unsigned)n_blocks), t(kRopeThreads);
