@@ -663,10 +663,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // a partial to the unit's last scratch slot.  One workgroup per unit of the launch; wave
 // w holds query rows 32*w .. 32*w+31 of the unit.
 constexpr int kTailWaves = 4;
+// Unit (launch numbering) and part of a tail or combine workgroup: by the unit's producing
+// XCD when the launch maps them (the hardware deals workgroup g to XCD g mod 8), else in
+// order.  False: no unit for this workgroup.
+__device__ __forceinline__ bool unit_of_wg(const SkLaunch& a, int total_units, int split, int& ug, int& part) {
+  if (a.xcd_map) {
+    const int x = (int)(wg_x() & 7u), j = (int)(wg_x() >> 3);
+    ug = a.xcd_first[x] + j / split;
+    part = j % split;
+    return ug < a.xcd_first[x + 1];
+  }
+  ug = (int)wg_x() / split;
+  part = (int)wg_x() % split;
+  return ug < total_units;
+}
+
 __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaunch a, int total_units) {
   __shared__ __attribute__((aligned(16))) char st[STAGE];
-  const int ug = wg_x();
-  if (ug >= total_units) return;
+  int ug, part_unused;
+  if (!unit_of_wg(a, total_units, 1, ug, part_unused)) return;
   int si, u;
   decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
@@ -781,10 +796,7 @@ static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kC
 // the tail), and writes the normalised output.  kCombSplit workgroups per unit, each
 // owning kCombRows rows; a thread owns 4 columns of kCombPer rows.  Partials are read
 // kCombBatch at a time, all loads in flight before the first is used.
-__global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units) {
-  const int ug = wg_x() / kCombSplit;
-  const int part = wg_x() % kCombSplit;
-  if (ug >= total_units) return;
+__global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units, int n_wg) {
   // A record written by this launch (one session): the attention read its keys from the
   // source, so the copy into the buffer can wait until now; its loads overlap the loads
   // of the partials below.
@@ -797,7 +809,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
     const u32x4* __restrict__ sv = reinterpret_cast<const u32x4*>(S0.rec_v);
     u32x4* __restrict__ dk = reinterpret_cast<u32x4*>(const_cast<void*>(S0.k)) + dst0;
     u32x4* __restrict__ dv = reinterpret_cast<u32x4*>(const_cast<void*>(S0.v)) + dst0;
-    const size_t nthr = (size_t)total_units * kCombSplit * kCombThreads;  // the whole grid
+    const size_t nthr = (size_t)n_wg * kCombThreads;  // the whole grid
     for (size_t i = (size_t)wg_x() * kCombThreads + tid_x(); i < n16; i += nthr) {
       const u32x4 x = __builtin_nontemporal_load(sk + i);
       const u32x4 y = __builtin_nontemporal_load(sv + i);
@@ -805,6 +817,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
       __builtin_nontemporal_store(y, dv + i);
     }
   }
+  int ug, part;
+  if (!unit_of_wg(a, total_units, kCombSplit, ug, part)) return;
   int si, u;
   decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
@@ -893,13 +907,14 @@ hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
-  launch(attn_tail_kernel, dim3(total_units), dim3(kTailWaves * 64), stream, a, total_units);
+  const int grid = a.xcd_map ? 8 * a.xcd_per : total_units;
+  launch(attn_tail_kernel, dim3(grid), dim3(kTailWaves * 64), stream, a, total_units);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
-  launch(combine_sk_kernel, dim3(total_units * kCombSplit), dim3(kCombThreads), stream, a,
-                     total_units);
+  const int grid = (a.xcd_map ? 8 * a.xcd_per : total_units) * kCombSplit;
+  launch(combine_sk_kernel, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
   return hipGetLastError();
 }
 

@@ -683,6 +683,40 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.part_o = reinterpret_cast<float*>(base);
       s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
     }
+    // Producing XCD of every unit (the attention kernel deals range w to XCD w / (G/8)
+    // when G is a multiple of 8): the XCD of the workgroup holding the unit's first tile;
+    // a unit without full tiles goes with the unit before it.
+    a.xcd_map = 0;
+    if (G >= 8 && G % 8 == 0 && iters > 0) {
+      int64_t count[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int x_prev = 0;
+      for (int i = 0; i < cnt; ++i) {
+        const sf::SkSession& s = a.s[i];
+        const int64_t units = (int64_t)H * s.qtiles;
+        for (int64_t u = 0; u < units; ++u) {
+          int x = x_prev;
+          if (s.ntiles > 0) {
+            const int64_t X = (int64_t)s.cost_begin + u * (s.ntiles + piece_cost) + piece_cost;
+            const int64_t w = ((X + 1) * G - 1) / cost;
+            x = (int)(w / (G / 8));
+          }
+          x = x < x_prev ? x_prev : (x > 7 ? 7 : x);
+          x_prev = x;
+          ++count[x];
+        }
+      }
+      a.xcd_first[0] = 0;
+      int64_t per = 0;
+      for (int x = 0; x < 8; ++x) {
+        a.xcd_first[x + 1] = a.xcd_first[x] + (int32_t)count[x];
+        per = count[x] > per ? count[x] : per;
+      }
+      a.xcd_per = (int32_t)per;
+      // only when the XCDs hold about the same number of units: otherwise the busiest one
+      // would serialize the tail and combine launches
+      const int64_t mean = (units_total + 7) / 8;
+      a.xcd_map = 4 * per <= 5 * mean ? 1 : 0;
+    }
     if (planning(arena)) continue;
     hipError_t e = hipSuccess;
     if (iters > 0) {

@@ -125,7 +125,12 @@ struct SkLaunch {
   // total_cost = T.  Workgroup w starts at the iteration of cost floor(w*T/G).
   int32_t piece_cost;
   int32_t total_cost;
-  int32_t pad[1];
+  // The tail and combine kernels take a unit on the XCD whose workgroups produced its
+  // pieces (xcd_map = 1), so the partials are read from that XCD's L2: workgroup g serves
+  // units xcd_first[g & 7] .. xcd_first[(g & 7) + 1] - 1, xcd_per per XCD at most.
+  int32_t xcd_map;
+  int32_t xcd_per;
+  int32_t xcd_first[9];
   SkSession s[kMaxLaunchSessions];
 };
 // Piece slots per unit a session of capacity C needs (bounded because a workgroup
