@@ -14,9 +14,10 @@
 //   attn_sk_kernel: the full tiles of all units of the launch, in order, are cut
 //     into G contiguous ranges, one per persistent workgroup (G = two 4-wave
 //     workgroups per CU).  The cut is made in cost units: a unit costs its tiles
-//     plus a fixed charge for its piece overhead (prologue and stream merge, about
-//     five tiles' worth), so a range that crosses into another unit holds fewer
-//     tiles and every workgroup finishes at about the same time.  Consecutive
+//     plus a fixed charge for its piece overhead (prologue and stream merge: seven
+//     tiles, the best of the charges measured), so a range that crosses into
+//     another unit holds fewer tiles and every workgroup finishes at about the
+//     same time.  Consecutive
 //     ranges share a head, and the grid is remapped so each XCD (the hardware deals
 //     workgroups round robin over the 8 XCDs) owns a contiguous eighth: a head's K/V
 //     stays in one XCD's L2.  The part of a unit inside one workgroup's range is a

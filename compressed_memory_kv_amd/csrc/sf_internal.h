@@ -85,7 +85,7 @@ constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
 constexpr int kSkMinRange = 8;      // fewest cost units a workgroup is given
 constexpr int kSkWgPerCu = 2;       // persistent workgroups per CU
-constexpr int kSkPieceCost = 5;     // a piece's fixed overhead, in tiles
+constexpr int kSkPieceCost = 7;     // a piece's fixed overhead, in tiles (tuned: 5, 7, 9, 12 measured)
 constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
