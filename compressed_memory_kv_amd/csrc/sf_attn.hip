@@ -12,12 +12,13 @@
 //
 // bf16 kernel (attn_bf16_kernel<D>, D = head_dim 64 or 128)
 //   workgroup = 4 waves = 128 query rows of one head; wave = 32 query rows.
-//   Keys go in tiles of 64 rows; K and V tiles go from global memory straight
+//   Keys go in tiles of 64 rows (32 at head_dim 128, where three workgroups share
+//   a CU); K and V tiles go from global memory straight
 //   into LDS (buffer_load_dwordx4 ... lds: a scalar tile offset plus a lane
 //   offset fixed for the unit, no staging registers), double buffered in two
 //   LDS arrays, as XOR-swizzled 16-byte chunks so MFMA operand reads are
 //   bank-conflict free.  Per tile and wave:
-//     S^T (64 keys x 32 queries) = K_tile . Q^T   on v_mfma_f32_32x32x16_bf16
+//     S^T (tile keys x 32 queries) = K_tile . Q^T on v_mfma_f32_32x32x16_bf16
 //       (A = K rows from LDS, B = Q held in VGPRs for the whole loop), so each
 //       lane owns one query and 32 of its scores: the row max is in-lane plus
 //       one exchange with lane^32;
@@ -61,7 +62,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int BM = kBf16RowsPerTile;  // 128 query rows per workgroup
-constexpr int BN = kBf16KeysPerTile;  // 64 keys per tile
+// Keys per tile: 64 at head_dim 64; 32 at head_dim 128, whose smaller stages (32 KB for
+// both) and leaner registers let three workgroups share a CU (three waves per SIMD).
+template <int D>
+constexpr int kTileKeys = D == 128 ? 32 : kBf16KeysPerTile;
+template <int D>
+constexpr int kWavesPerEu = D == 128 ? 3 : 1;
 static_assert(BM == kWaves * 32, "one 32-row MFMA block per wave");
 
 // Work unit of this workgroup: XCD-aware remap of the workgroup id; the grid is
@@ -135,7 +141,7 @@ __device__ __forceinline__ int key_row(const Unit& u, int kappa) {
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
-// LDS tile geometry: one stage holds a K tile then a V tile, BN rows of 2D bytes
+// LDS tile geometry: one stage holds a K tile then a V tile, kTileKeys rows of 2D bytes
 // each, as 16-byte chunks permuted within each row so that the MFMA operand reads
 // are bank-conflict free on the 64 banks (256 bytes per cycle) of gfx950's LDS:
 //   K: chunk c of row r sits at c ^ ksw(r).  A ds_read_b128 serves 16 lanes (16
@@ -148,7 +154,7 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 template <int D>
 struct Tile {
   static constexpr int ROW = 2 * D;              // bytes per row
-  static constexpr int KBYTES = BN * ROW;
+  static constexpr int KBYTES = kTileKeys<D> * ROW;
   static constexpr int STAGE = 2 * KBYTES;       // K tile then V tile
   static __device__ __forceinline__ int ksw(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
   static __device__ __forceinline__ int vsw(int r) { return D == 64 ? 2 * (r & 3) : 4 * (r & 3); }
@@ -174,7 +180,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char* p) {
 constexpr float kSumLimit = 32768.0f;
 
 template <int D, bool BIAS>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<D>)))
+void attn_bf16_kernel(const AttnLaunch a) {
+  constexpr int BN = kTileKeys<D>;
+  constexpr int KB = BN / 32;                // 32-key MFMA blocks per tile
   using T = Tile<D>;
   constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;             // MFMA k-steps over head_dim
@@ -307,69 +316,73 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
 
   // One tile of work on the stage at byte offset ST.
   auto compute_tile = [&](const int tile, const char* st) {
-    // ---- S^T = K . Q^T : two 32-key blocks
-    f32x16 s0, s1;
+    // ---- S^T = K . Q^T : KB 32-key blocks
+    f32x16 sb[KB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[b][r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kaddr[kk]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + kaddr[kk] + 32 * T::ROW);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const bf16x8 ab = *reinterpret_cast<const bf16x8*>(st + kaddr[kk] + 32 * b * T::ROW);
+        sb[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, qreg[kk], sb[b], 0, 0, 0);
+      }
     }
     // ---- keys past the end of this unit's range (ragged last tile) score -inf
     if (tile * BN + BN > key_hi) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kb = tile * BN + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (kb >= key_hi) s0[r] = -INFINITY;
-        if (kb + 32 >= key_hi) s1[r] = -INFINITY;
-      }
+      for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kb = tile * BN + 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kb >= key_hi) sb[b][r] = -INFINITY;
+        }
     }
     // ---- recency bias: scores to log2 units with each key's bias added (register r of
     // block b holds key 32b + 8(r/4) + 4g + r%4); from here on the scale is 1.
     if constexpr (BIAS) {
       const float* bs = reinterpret_cast<const float*>(st + BIAS_OFF);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 b0 = *reinterpret_cast<const float4*>(bs + 8 * q4 + 4 * g);
-        const float4 b1 = *reinterpret_cast<const float4*>(bs + 32 + 8 * q4 + 4 * g);
-        s0[4 * q4 + 0] = __builtin_fmaf(s0[4 * q4 + 0], c, b0.x);
-        s0[4 * q4 + 1] = __builtin_fmaf(s0[4 * q4 + 1], c, b0.y);
-        s0[4 * q4 + 2] = __builtin_fmaf(s0[4 * q4 + 2], c, b0.z);
-        s0[4 * q4 + 3] = __builtin_fmaf(s0[4 * q4 + 3], c, b0.w);
-        s1[4 * q4 + 0] = __builtin_fmaf(s1[4 * q4 + 0], c, b1.x);
-        s1[4 * q4 + 1] = __builtin_fmaf(s1[4 * q4 + 1], c, b1.y);
-        s1[4 * q4 + 2] = __builtin_fmaf(s1[4 * q4 + 2], c, b1.z);
-        s1[4 * q4 + 3] = __builtin_fmaf(s1[4 * q4 + 3], c, b1.w);
-      }
+      for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 bb = *reinterpret_cast<const float4*>(bs + 32 * b + 8 * q4 + 4 * g);
+          sb[b][4 * q4 + 0] = __builtin_fmaf(sb[b][4 * q4 + 0], c, bb.x);
+          sb[b][4 * q4 + 1] = __builtin_fmaf(sb[b][4 * q4 + 1], c, bb.y);
+          sb[b][4 * q4 + 2] = __builtin_fmaf(sb[b][4 * q4 + 2], c, bb.z);
+          sb[b][4 * q4 + 3] = __builtin_fmaf(sb[b][4 * q4 + 3], c, bb.w);
+        }
     }
     const float cs = BIAS ? 1.0f : c;
     // ---- P = exp2(S*c - mref) in bf16 and its row sum, against the current reference.
-    bf16x8 pb[4];
+    bf16x8 pb[2 * KB];
     float ts;
     auto probs = [&]() {
-      float part[4];
+      float part[2 * KB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16& sj = j < 2 ? s0 : s1;
+      for (int j = 0; j < 2 * KB; ++j) {
         float e[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[8 * (j & 1) + r], cs, -mref));
+        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j >> 1][8 * (j & 1) + r], cs, -mref));
 #pragma unroll
         for (int r = 0; r < 8; ++r) pb[j][r] = (__bf16)e[r];
         part[j] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
-      ts = (part[0] + part[1]) + (part[2] + part[3]);
+      ts = part[0];
+#pragma unroll
+      for (int j = 1; j < 2 * KB; ++j) ts += part[j];
     };
     probs();
     // ---- the reference moves only when some p left its range, and on the unit's first
     // tile (the reference is -inf before it; masked keys there give NaN p, discarded here).
     if (tile == t0 || __any(ts > kSumLimit)) {
-      float mt = fmaxf(s0[0], s1[0]);
+      float mt = fmaxf(sb[0][0], sb[0][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = max3(mt, s0[r], s1[r]);
+      for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = max3(mt, sb[b][r], sb[b][r + 1]);
       mt = fmaxf(mt, xor32(mt)) * cs;
       const float mnew = fmaxf(mref, mt);
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnLaunch a)
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2 * KB; ++j) {
         const int roff = (32 * (j >> 1) + 16 * (j & 1)) * T::ROW;
         const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff));
         const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff + 8 * T::ROW));
