@@ -10,19 +10,22 @@
 //
 // Work decomposition.  A unit is (session, head, 128-row query tile).  Its keys
 // are floor(keys/64) full 64-key tiles plus, when keys is not a multiple of 64,
-// a tail of fewer than 64 keys.
-//   attn_sk_kernel: the full tiles of all units of the launch, in order, are cut
-//     into G contiguous ranges, one per persistent workgroup (G = two 4-wave
-//     workgroups per CU).  The cut is made in cost units: a unit costs its tiles
-//     plus a fixed charge for its piece overhead (prologue and stream merge: seven
-//     tiles, the best of the charges measured), so a range that crosses into
-//     another unit holds fewer tiles and every workgroup finishes at about the
-//     same time.  Consecutive
-//     ranges share a head, and the grid is remapped so each XCD (the hardware deals
-//     workgroups round robin over the 8 XCDs) owns a contiguous eighth: a head's K/V
-//     stays in one XCD's L2.  The part of a unit inside one workgroup's range is a
-//     "piece"; a piece that is the whole unit (and the unit has no tail) writes the
-//     output, otherwise it writes an unnormalised partial (O, reference max, row
+// a tail of fewer than 64 keys.  The units of one (session, head), a "column", share
+// those tiles.
+//   attn_sk_kernel: persistent 4-wave workgroups, two per CU, form groups of as
+//     many members as a session has query tiles (9 at 1104 rows), each XCD holding
+//     whole groups (the hardware deals workgroups round robin over the 8 XCDs, and
+//     the grid is remapped so each XCD owns a contiguous eighth).  The full tiles of
+//     all columns of the launch, in order, are cut into one contiguous range per
+//     group; every member walks the group's range for its own query tile, so the
+//     members read each K/V tile at about the same time and it comes from HBM once
+//     (the rest from the XCD's L2), at the start of a range too.  The cut is made in
+//     cost units: a column costs its tiles plus a fixed charge for its piece overhead
+//     (prologue and stream merge: seven tiles, the best of the charges measured), so
+//     a range that crosses into another column holds fewer tiles and every group
+//     finishes at about the same time.  The part of a unit inside one group's range
+//     is a "piece"; a piece that is the whole unit (and the unit has no tail) writes
+//     the output, otherwise it writes an unnormalised partial (O, reference max, row
 //     sum) to the session's scratch;
 //   attn_tail_kernel: one workgroup per unit with a tail writes the tail's
 //     partial to the unit's last scratch slot;
@@ -129,32 +132,34 @@ __device__ __forceinline__ int session_of_iter(const SkLaunch& a, int it) {
   return __builtin_amdgcn_readfirstlane(si);
 }
 
-// Ranges are cut in cost units (a unit costs piece_cost, then one per tile), so a
-// workgroup whose range crosses into another unit gets fewer tiles.  pos(C): the
-// iteration at cost C (the piece_cost of a unit maps to its first tile).
-__device__ __forceinline__ int range_start(const SkLaunch& a, const int w) {
-  if (w >= a.n_wg) return a.n_iters;
-  const long long C = (long long)w * a.total_cost / a.n_wg;
+// Group ranges are cut in cost units: a column costs mult * (piece_cost + its tiles), and
+// tile t of a column sits at cost mult * (piece_cost + t) from the column's start.  Group
+// g starts at the first tile at or past cost floor(g*T/NG).
+__device__ __forceinline__ int range_start(const SkLaunch& a, const int g) {
+  if (g >= a.n_grp) return a.n_iters;
+  const long long C = (long long)g * a.total_cost / a.n_grp;
   int si = 0;
   for (int i = 0; i < a.n_sessions; ++i)
     if (a.s[i].ntiles > 0 && a.s[i].cost_begin <= C) si = i;
   si = __builtin_amdgcn_readfirstlane(si);
   const SkSession& S = a.s[si];
-  const long long per = S.ntiles + a.piece_cost;
+  const long long m = S.mult;
+  const long long per = m * (S.ntiles + a.piece_cost);
   const long long r0 = C - S.cost_begin;
-  const long long u = r0 / per;
-  const long long r = r0 - u * per - a.piece_cost;
-  return (int)(S.it_begin + u * S.ntiles + (r > 0 ? r : 0));
+  const long long col = r0 / per;
+  const long long t = (r0 - col * per + m - 1) / m - a.piece_cost;
+  return (int)(S.it_begin + col * S.ntiles + (t > 0 ? t : 0));
 }
 
-// Workgroup holding iteration i: the last w whose range starts at or before it.
-__device__ __forceinline__ int wg_of_iter(const SkLaunch& a, const int i) {
+// Group holding column iteration i: the last g whose range starts at or before it.
+__device__ __forceinline__ int grp_of_iter(const SkLaunch& a, const int i) {
   const SkSession& S = a.s[session_of_iter(a, i)];
   const int local = i - S.it_begin;
-  const int u = local / S.ntiles;
-  const long long X = (long long)S.cost_begin + (long long)u * (S.ntiles + a.piece_cost) + a.piece_cost +
-                      (local - u * S.ntiles);
-  return (int)(((X + 1) * a.n_wg - 1) / a.total_cost);
+  const int col = local / S.ntiles;
+  const long long m = S.mult;
+  const long long X = (long long)S.cost_begin + (long long)col * m * (S.ntiles + a.piece_cost) +
+                      m * (a.piece_cost + (local - col * S.ntiles));
+  return (int)(((X + 1) * a.n_grp - 1) / a.total_cost);
 }
 
 // Session and unit of a unit index counted over the whole launch.
@@ -259,10 +264,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
   __shared__ int redo[kWaves];
   const int G = a.n_wg;
-  const int N = a.n_iters;
   const int w = (G & 7) == 0 ? (int)(wg_x() & 7u) * (G >> 3) + (int)(wg_x() >> 3) : (int)wg_x();
-  const int it_lo = __builtin_amdgcn_readfirstlane(range_start(a, w));
-  const int it_hi = __builtin_amdgcn_readfirstlane(range_start(a, w + 1));
+  // group and member of this workgroup
+  const int GS = a.grp_size;
+  int grp, mem;
+  if (a.grp_per_xcd > 0) {
+    const int per = G >> 3, x = w / per, lw = w - x * per;
+    if (lw >= a.grp_per_xcd * GS) return;  // past the XCD's whole groups: no work
+    grp = x * a.grp_per_xcd + lw / GS;
+    mem = lw % GS;
+  } else {
+    grp = w / GS;
+    mem = w - grp * GS;
+    if (grp >= a.n_grp) return;
+  }
+  grp = __builtin_amdgcn_readfirstlane(grp);
+  mem = __builtin_amdgcn_readfirstlane(mem);
+  const int it_lo = __builtin_amdgcn_readfirstlane(range_start(a, grp));
+  const int it_hi = __builtin_amdgcn_readfirstlane(range_start(a, grp + 1));
   const int H = a.n_heads;
   const float c = a.scale_log2;
 
@@ -288,14 +307,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   SK_OPERAND_ADDRESSES(soff);
   const f32x16 zero16 = {};
 
-  // Q^T operands of the piece that starts at iteration it: query block qb holds rows
-  // qrow0 + 32*qb + l32 (rows past R read row R-1).  The next piece's are loaded as soon
-  // as the current piece's last S^T is done, so their latency hides behind the merge.
+  // Q^T operands of query tile qt of head h: query block qb holds rows qrow0 + 32*qb +
+  // l32 (rows past R read row R-1).  The next piece's are loaded as soon as the current
+  // piece's last S^T is done, so their latency hides behind the merge.
   bf16x8 q0[4], q1[4];
-  auto load_q = [&](const int it) {
-    const SkSession& S = a.s[session_of_iter(a, it)];
-    const int u = __builtin_amdgcn_readfirstlane((it - S.it_begin) / S.ntiles);
-    const int qt = u % S.qtiles, h = u / S.qtiles;
+  auto load_q = [&](const SkSession& S, const int h, const int qt) {
     const int qrow0 = qt * kSkRows + hw * 64;
     const int r0 = min(qrow0 + l32, S.rows - 1);
     const int r1 = min(qrow0 + 32 + l32, S.rows - 1);
@@ -307,27 +323,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       q1[kk] = *reinterpret_cast<const bf16x8*>(qp1 + 16 * kk);
     }
   };
-  if (it_lo < it_hi) load_q(it_lo);
+  // The first query tile this member takes in column iteration it (none: qtiles or more).
+  auto first_q = [&](const int it, int& qh) {
+    const SkSession& S = a.s[session_of_iter(a, it)];
+    qh = __builtin_amdgcn_readfirstlane((it - S.it_begin) / S.ntiles);
+    return mem < S.qtiles;
+  };
+  bool q_ok = false;  // q0 / q1 hold the Q of the next piece
+  if (it_lo < it_hi) {
+    int qh;
+    if (first_q(it_lo, qh)) {
+      load_q(a.s[session_of_iter(a, it_lo)], qh, mem);
+      q_ok = true;
+    }
+  }
 
   for (int it = it_lo; it < it_hi;) {
-    // ---- the piece: one unit's tiles [tile0, tile1) inside this workgroup's range
+    // ---- a column piece: tiles [tile0, tile1) of head h inside this group's range, for
+    // each of this member's query tiles
     const int si = session_of_iter(a, it);
     const SkSession& S = a.s[si];
     const int nt = S.ntiles;
     const int local = it - S.it_begin;
-    const int u = __builtin_amdgcn_readfirstlane(local / nt);
-    const int tile0 = __builtin_amdgcn_readfirstlane(local - u * nt);
+    const int h = __builtin_amdgcn_readfirstlane(local / nt);
+    const int tile0 = __builtin_amdgcn_readfirstlane(local - h * nt);
     const int tile1 = min(nt, tile0 + (it_hi - it));
-    const int qt = __builtin_amdgcn_readfirstlane(u % S.qtiles);
-    const int h = __builtin_amdgcn_readfirstlane(u / S.qtiles);
     const int n = tile1 - tile0;
     const int s_lo = tile0 + (stream * n) / kStreams;   // this stream's tiles [s_lo, s_hi)
     const int s_hi = tile0 + ((stream + 1) * n) / kStreams;
     const int steps = (n + kStreams - 1) / kStreams;
     const int row_stride = H * D;
     const int row_bytes = 2 * row_stride;
-    const int qrow0 = qt * kSkRows + hw * 64;
-    const bool wave_on = qrow0 < S.rows;
 
     int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
     seg_tables<REC>(S, seg_row, seg_key);
@@ -385,6 +411,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     };
 
+    // piece slot of the column's units: the k-th group of the column writes slot k
+    const int k = grp - grp_of_iter(a, S.it_begin + h * nt);
+    for (int qt = mem; qt < S.qtiles; qt += GS) {
+    const int u = h * S.qtiles + qt;
+    if (!q_ok) load_q(S, h, qt);
+    const int qrow0 = qt * kSkRows + hw * 64;
+    const bool wave_on = qrow0 < S.rows;
     f32x16 o00, o10, o01, o11;  // O^T blocks [d block][query block]
     float mref0, mref1, lsum0, lsum1, tsmax;
 
@@ -561,7 +594,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (!__builtin_amdgcn_readfirstlane(any_bad) || attempt == 1) break;
     }
 
-    if (it + (tile1 - tile0) < it_hi) load_q(it + (tile1 - tile0));  // the next piece's Q
+    // the next piece's Q: this member's next query tile of the column, else its first of
+    // the next column piece
+    q_ok = false;
+    if (qt + GS < S.qtiles) {
+      load_q(S, h, qt + GS);
+      q_ok = true;
+    } else if (it + n < it_hi) {
+      int qh;
+      if (first_q(it + n, qh)) {
+        load_q(a.s[session_of_iter(a, it + n)], qh, mem);
+        q_ok = true;
+      }
+    }
 
     // ---- merge the two streams (stream 0 collects), then write
     const int mlane = fresh_lane();
@@ -618,8 +663,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const float lt0 = l0 + xor32(l0), lt1 = l1 + xor32(l1);
       const bool has_tail = (S.n_keys & (BN - 1)) != 0;
       const bool whole = tile0 == 0 && tile1 == nt && !has_tail;
-      // piece slot of this unit: its k-th workgroup writes slot k
-      const int k = w - wg_of_iter(a, S.it_begin + u * nt);
       const int el32 = mlane & 31, eg = mlane >> 5;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -655,7 +698,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     __syncthreads();  // the merge buffer overlays the stages of the next piece
-    it += tile1 - tile0;
+    }
+    it += n;
   }
 }
 
@@ -824,14 +868,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
   const bool has_tail = (S.n_keys & (kSkKeys - 1)) != 0;
+  const int qt = u % S.qtiles, h = u / S.qtiles;
   int pieces = 0;
   if (S.ntiles > 0) {
-    const int first = S.it_begin + u * S.ntiles;
-    pieces = wg_of_iter(a, first + S.ntiles - 1) - wg_of_iter(a, first) + 1;
+    const int first = S.it_begin + h * S.ntiles;  // the column's first iteration
+    pieces = grp_of_iter(a, first + S.ntiles - 1) - grp_of_iter(a, first) + 1;
   }
   if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
   const int total = pieces + (has_tail ? 1 : 0);
-  const int qt = u % S.qtiles, h = u / S.qtiles;
   const int H = a.n_heads;
   constexpr int RSTRIDE = kCombThreads / (D / 4);  // 16 rows between a thread's rows
   const int r0 = part * kCombRows + tid_x() / (D / 4);
@@ -887,8 +931,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
 }  // namespace
 
 int32_t sk_pieces_per_unit(int64_t capacity_rows) {
-  // pieces of a unit: at most ceil(tiles / kSkMinRange) + 1 (a workgroup range that
-  // starts inside a unit holds at least kSkMinRange of its tiles); one more slot for
+  // pieces of a unit: at most ceil(tiles / kSkMinRange) + 1 (a group range that
+  // starts inside a column holds at least kSkMinRange of its tiles); one more slot for
   // the tail
   const int64_t nt = capacity_rows / kSkKeys;
   return (int32_t)((nt + kSkMinRange - 1) / kSkMinRange + 2);

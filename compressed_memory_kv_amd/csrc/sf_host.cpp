@@ -611,6 +611,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     int64_t iters = 0, units_total = 0, cost = 0;
     const int piece_cost = sf::kSkPieceCost;
     bool any_tail = false;
+    int64_t qmax = 1;
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       Segs sg;
@@ -641,34 +642,66 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.qtiles = (int32_t)((b->geo.R + sf::kSkRows - 1) / sf::kSkRows);
       s.ntiles = (int32_t)(sg.keys / sf::kSkKeys);
       any_tail = any_tail || (sg.keys % sf::kSkKeys) != 0;
-      const int64_t units = (int64_t)H * s.qtiles;
+      units_total += (int64_t)H * s.qtiles;
+      qmax = s.qtiles > qmax ? s.qtiles : qmax;
+    }
+    // Groups of workgroups sharing key ranges, one query tile per member: as many members as
+    // the most query tiles of a session, at most one XCD's share of the workgroups, whole
+    // groups on each XCD (the hardware deals workgroup g to XCD g mod 8).
+    int64_t G = (int64_t)sf::kSkWgPerCu * device_cu_count();
+    if (G >= 8) G -= G % 8;
+    if (G < 1) G = 1;
+    const bool by_xcd = G >= 8 && G % 8 == 0;
+    const int64_t per_x = by_xcd ? G / 8 : G;
+    const int64_t GS = qmax < per_x ? qmax : per_x;
+    int64_t gpx = by_xcd ? per_x / GS : 0;
+    int64_t NG = by_xcd ? 8 * gpx : G / GS;
+    int64_t mmax = 1;
+    for (int i = 0; i < cnt; ++i) {
+      sf::SkSession& s = a.s[i];
+      s.mult = (int32_t)((s.qtiles + GS - 1) / GS);
+      mmax = s.mult > mmax ? s.mult : mmax;
       s.it_begin = (int32_t)iters;
       s.cost_begin = (int32_t)cost;
-      iters += units * s.ntiles;
-      cost += s.ntiles > 0 ? units * (s.ntiles + piece_cost) : 0;
-      units_total += units;
+      iters += (int64_t)H * s.ntiles;
+      cost += s.ntiles > 0 ? (int64_t)H * s.mult * (s.ntiles + piece_cost) : 0;
     }
     if (iters >= ((int64_t)1 << 30) || units_total >= ((int64_t)1 << 28) || cost >= ((int64_t)1 << 31))
       return fail(b0, SF_E_UNSUPPORTED, "attention launch too large");
-    int64_t G = (int64_t)sf::kSkWgPerCu * device_cu_count();
-    if (G > iters / sf::kSkMinRange) G = iters / sf::kSkMinRange;
-    if (G < 1) G = 1;
-    if (G >= 8) G -= G % 8;
+    // Every group range spans at least mmax * kSkMinRange cost units (so at least
+    // kSkMinRange tiles of any column it starts inside); with fewer, fewer groups, laid out
+    // in order.
+    if (NG > cost / (sf::kSkMinRange * mmax)) {
+      NG = cost / (sf::kSkMinRange * mmax);
+      if (NG < 1) NG = 1;
+      gpx = 0;
+      G = NG * GS;
+    }
     a.n_wg = (int32_t)G;
+    a.n_grp = (int32_t)NG;
+    a.grp_size = (int32_t)GS;
+    a.grp_per_xcd = (int32_t)gpx;
     a.n_iters = (int32_t)iters;
     a.piece_cost = piece_cost;
     a.total_cost = (int32_t)cost;
-    // Partial-result slots per unit: every workgroup range spans at least floor(T / G)
-    // cost units, and one that starts past a unit's first tile holds that many tiles of
-    // it, so a unit of ntiles tiles meets at most ceil(ntiles / floor(T / G)) + 1 ranges;
-    // one more slot for the tail.  G <= N / kSkMinRange and T >= N make floor(T / G) >=
-    // kSkMinRange (or G = 1 and one range holds every tile), so this never exceeds the
-    // capacity bound the session's own scratch region is sized for.
-    const int64_t per_wg = cost / G > 0 ? cost / G : 1;
+    // Group holding tile t of column col of a session, as the attention kernel finds it.
+    auto grp_of = [&](const sf::SkSession& s, int64_t col, int64_t t) -> int64_t {
+      const int64_t m = s.mult;
+      const int64_t X = (int64_t)s.cost_begin + col * m * (s.ntiles + piece_cost) + m * (piece_cost + t);
+      return ((X + 1) * NG - 1) / (cost > 0 ? cost : 1);
+    };
+    // Partial-result slots per unit: the groups its column meets, then one for the tail.
+    // A group range holds at least kSkMinRange tiles of a column it starts inside, so this
+    // never exceeds the capacity bound the session's own scratch region is sized for.
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       sf::SkSession& s = a.s[i];
-      s.ppu = (int32_t)((s.ntiles + per_wg - 1) / per_wg + 2);
+      int64_t pieces = 0;
+      for (int64_t h = 0; s.ntiles > 0 && h < H; ++h) {
+        const int64_t p = grp_of(s, h, s.ntiles - 1) - grp_of(s, h, 0) + 1;
+        pieces = p > pieces ? p : pieces;
+      }
+      s.ppu = (int32_t)(pieces + 1);
       if (s.ppu > sf::sk_pieces_per_unit(b->geo.C))
         return fail(b0, SF_E_UNSUPPORTED, "internal: stream-K partial slots exceed the session's scratch bound");
       const int64_t units = (int64_t)H * s.qtiles;
@@ -683,11 +716,11 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.part_o = reinterpret_cast<float*>(base);
       s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
     }
-    // Producing XCD of every unit (the attention kernel deals range w to XCD w / (G/8)
-    // when G is a multiple of 8): the XCD of the workgroup holding the unit's first tile;
-    // a unit without full tiles goes with the unit before it.
+    // Producing XCD of every unit (with whole groups per XCD, group g is on XCD
+    // g / grp_per_xcd): the XCD of the group holding its column's first tile; a unit
+    // without full tiles goes with the unit before it.
     a.xcd_map = 0;
-    if (G >= 8 && G % 8 == 0 && iters > 0) {
+    if (gpx > 0 && iters > 0) {
       int64_t count[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       int x_prev = 0;
       for (int i = 0; i < cnt; ++i) {
@@ -695,11 +728,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
         const int64_t units = (int64_t)H * s.qtiles;
         for (int64_t u = 0; u < units; ++u) {
           int x = x_prev;
-          if (s.ntiles > 0) {
-            const int64_t X = (int64_t)s.cost_begin + u * (s.ntiles + piece_cost) + piece_cost;
-            const int64_t w = ((X + 1) * G - 1) / cost;
-            x = (int)(w / (G / 8));
-          }
+          if (s.ntiles > 0) x = (int)(grp_of(s, u / s.qtiles, 0) / gpx);
           x = x < x_prev ? x_prev : (x > 7 ? 7 : x);
           x_prev = x;
           ++count[x];

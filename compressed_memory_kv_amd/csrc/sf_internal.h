@@ -75,17 +75,19 @@ struct AttnLaunch {
 };
 
 // ---- persistent stream-K attention (bf16, head_dim 64) ----------------------
-// The launch's work is the flattened sequence of (session, head, 128-row query
-// tile, full 64-key tile) iterations; workgroup w takes the iterations between
-// costs floor(w*T/G) and floor((w+1)*T/G) (see SkLaunch::piece_cost).  A query tile that spans several workgroups leaves one
-// partial result per workgroup ("piece") in its session's scratch; keys past the
-// last full tile (the tail) leave one more, from the tail kernel, in the unit's
-// last slot; the combine kernel merges them.
+// A unit is (session, head, 128-row query tile); a column is (session, head), the
+// full 64-key tiles its units share.  The launch's work is the flattened sequence of
+// (session, head, tile) column iterations; group g of workgroups takes the iterations
+// between costs floor(g*T/NG) and floor((g+1)*T/NG) (see SkLaunch::piece_cost), each
+// member of the group the same iterations for its own query tiles.  A unit whose tiles
+// span several groups leaves one partial result per group ("piece") in its session's
+// scratch; keys past the last full tile (the tail) leave one more, from the tail kernel,
+// in the unit's last slot; the combine kernel merges them.
 constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
-constexpr int kSkMinRange = 8;      // fewest cost units a workgroup is given
+constexpr int kSkMinRange = 8;      // fewest tiles of a column a group range starting inside it holds
 constexpr int kSkWgPerCu = 2;       // persistent workgroups per CU
-constexpr int kSkPieceCost = 7;     // a piece's fixed overhead, in tiles (tuned: 5, 7, 9, 12 measured)
+constexpr int kSkPieceCost = 7;     // a piece's fixed overhead, in tiles (tuned: 4, 5, 7, 9, 12 measured)
 constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
@@ -108,21 +110,24 @@ struct SkSession {
   int32_t qtiles;       // ceil(rows / kSkRows)
   int32_t ntiles;       // full key tiles: n_keys / kSkKeys
   int32_t ppu;          // piece slots per unit in the scratch
-  int32_t it_begin;     // first iteration of this session in the launch
+  int32_t it_begin;     // first column iteration of this session in the launch
   int32_t cost_begin;   // first cost unit of this session (see SkLaunch::piece_cost)
-  int32_t pad[2];
+  int32_t mult;         // units of a column one workgroup of a group takes: ceil(qtiles / grp_size)
+  int32_t pad;
   int32_t seg_begin[SF_MAX_SEGMENTS];
   int32_t seg_len[SF_MAX_SEGMENTS];
 };
 struct SkLaunch {
   int32_t n_sessions;
   int32_t n_heads;
-  int32_t n_wg;         // G
-  int32_t n_iters;      // N
+  int32_t n_wg;         // workgroups of the launch
+  int32_t n_iters;      // N, column iterations
   float scale_log2;
-  // Workgroup ranges are cut in cost units: a unit of ntiles full tiles costs
-  // ntiles + piece_cost (its piece overhead, in tiles), a unit without full tiles 0;
-  // total_cost = T.  Workgroup w starts at the iteration of cost floor(w*T/G).
+  // Group ranges are cut in cost units: a column of ntiles full tiles costs
+  // mult * (ntiles + piece_cost) (piece_cost: a piece's overhead, in tiles; mult: the
+  // units of the column one member takes), a column without full tiles 0; total_cost = T.
+  // Tile t of a column sits at cost mult * (piece_cost + t) from the column's start, and
+  // group g starts at the first tile at or past cost floor(g*T/NG).
   int32_t piece_cost;
   int32_t total_cost;
   // The tail and combine kernels take a unit on the XCD whose workgroups produced its
@@ -131,10 +136,18 @@ struct SkLaunch {
   int32_t xcd_map;
   int32_t xcd_per;
   int32_t xcd_first[9];
+  // Groups: grp_size workgroups take the same key ranges, one query tile each (tile qt of
+  // a column goes to member qt mod grp_size), so a K/V tile is fetched once for the group.
+  // n_grp groups; the ranges above are cut per group (n_grp takes the place of G).  With
+  // grp_per_xcd > 0 each XCD holds grp_per_xcd whole groups (logical workgroups of an XCD
+  // past them take no work); 0: group g is logical workgroups g*grp_size ...
+  int32_t n_grp;
+  int32_t grp_size;
+  int32_t grp_per_xcd;
   SkSession s[kMaxLaunchSessions];
 };
-// Piece slots per unit a session of capacity C needs (bounded because a workgroup
-// range that starts inside a unit holds at least kSkMinRange of its tiles).
+// Piece slots per unit a session of capacity C needs (bounded because a group range
+// that starts inside a column holds at least kSkMinRange of its tiles).
 int32_t sk_pieces_per_unit(int64_t capacity_rows);
 size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows);
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream);

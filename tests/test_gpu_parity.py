@@ -191,6 +191,67 @@ def test_batched_sessions_ragged():
             say(f"   s{si} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
 
 
+def _replay(wl, si, t_end, rows_for_oracle=True):
+    """A one-block session replayed to frame t_end (explicit eviction, then the write), with
+    its oracle."""
+    g = so.Geometry.from_workload(wl)
+    sess = new_session(wl)
+    orc = so.MemoryReplay(g)
+    for t in range(t_end + 1):
+        if t >= 1:
+            sess.evict(t)
+        _, k, v = sf_inputs.frame_tensors(wl, si, 0, t, device="cuda")
+        sess.write_record(0, t, k, v)
+        orc.step(t, {0: (host(k), host(v))})
+    torch.cuda.synchronize()
+    check_tables(sess, orc, f"mixed session {si}")
+    return g, sess, orc
+
+
+@needs_gpu
+@pytest.mark.timeout(600)
+def test_batched_mixed_geometries():
+    """One batched read over sessions whose records differ in size: 1, 3, 9 and 13 query tiles
+    (workgroup groups of 13 members, most idle for the smaller sessions), key counts with and
+    without a tail; then one session of 65 query tiles, more than one XCD's workgroups, so a
+    group member takes two query tiles of a column.  Every session against the oracle."""
+    base = dict(y=2, w=6, n_heads=16, head_dim=64, n_blocks=1, dtype="bf16", v_scale=1.0)
+    shapes = [(100, 28, 3), (280, 20, 5), (1008, 96, 8), (1500, 100, 6)]  # (hw, x, frame)
+    wls, sessions, oracles, geos = [], [], [], []
+    for si, (hw, x, t_end) in enumerate(shapes):
+        wl = dict(base, hw=hw, x=x, frames=list(range(t_end + 1)), seed=40 + si)
+        say(f"[mixed] replay session {si}: R={hw + x}, to t={t_end}")
+        g, sess, orc = _replay(wl, si, t_end)
+        wls.append(wl)
+        sessions.append(sess)
+        oracles.append(orc)
+        geos.append(g)
+    qs = [sf_inputs.frame_tensors(wl, si, 0, wl["frames"][-1], device="cuda")[0] for si, wl in enumerate(wls)]
+    outs = [out_like(wl) for wl in wls]
+    say("[mixed] batched attend")
+    sf.attend_batch(sessions, 0, qs, outs)
+    torch.cuda.synchronize()
+    for si, (orc, g) in enumerate(zip(oracles, geos)):
+        rows = None if g.r <= 1104 else np.unique(np.concatenate([np.arange(0, g.r, 7), np.arange(g.r - 70, g.r)]))
+        ref = orc.attend(0, host(qs[si]), rows=rows)
+        got = outs[si] if rows is None else outs[si][torch.from_numpy(rows).cuda()]
+        ma, rel = check_attention(got, ref, "bf16", f"mixed s{si} R={g.r} keys={orc.n_keys()}")
+        say(f"   s{si} R={g.r} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
+
+    # 8320 rows = 65 query tiles; Y = 1, W = 2: frame 1 reads 16,640 keys
+    wl = dict(base, hw=8192, x=128, y=1, w=2, frames=[0, 1], seed=47)
+    say("[mixed] replay the 65-tile session")
+    g, sess, orc = _replay(wl, 0, 1)
+    q = sf_inputs.frame_tensors(wl, 0, 0, 1, device="cuda")[0]
+    out = out_like(wl)
+    sess.attend(0, q, out)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, g.r, 61), np.arange(8192 - 8, g.r, 3)]))
+    ref = orc.attend(0, host(q), rows=rows)
+    ma, rel = check_attention(out[torch.from_numpy(rows).cuda()], ref, "bf16", "65-tile session")
+    say(f"   R={g.r} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
+
+
 @needs_gpu
 @pytest.mark.timeout(900)
 def test_rollout_28_blocks_64_frames():
