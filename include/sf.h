@@ -250,7 +250,7 @@ sf_status sf_attend(sf_buffer* const* bufs, int32_t n, int32_t block, const void
  * address is looked up (hipGetSymbolAddress) on the first call on each device, with that
  * device current.  A read whose scratch does not fit (the whole batch's, laid out one session
  * after another) returns SF_E_UNSUPPORTED and enqueues nothing; a served read (16 heads of 64,
- * 1,104 query rows, 6,528 keys) takes about 29.2 MB.  Every call on a GPU shares that GPU's
+ * 1,104 query rows, 6,528 keys) takes about 24.3 MB.  Every call on a GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, other threads) race and give
  * undefined results; calls ordered on one stream are safe.  Nothing in the array needs to
  * start at zero: each call writes every slot it reads. */
