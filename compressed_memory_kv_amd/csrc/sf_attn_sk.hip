@@ -135,31 +135,38 @@ __device__ __forceinline__ int session_of_iter(const SkLaunch& a, int it) {
 // Group ranges are cut in cost units: a column costs mult * (piece_cost + its tiles), and
 // tile t of a column sits at cost mult * (piece_cost + t) from the column's start.  Group
 // g starts at the first tile at or past cost floor(g*T/NG).
-__device__ __forceinline__ int range_start(const SkLaunch& a, const int g) {
-  if (g >= a.n_grp) return a.n_iters;
-  const long long C = (long long)g * a.total_cost / a.n_grp;
+// I: the integer type the formulas run in (unsigned when SkLaunch::narrow holds; each
+// kernel that uses them is built for both and the launch picks one).
+template <typename I>
+__device__ __forceinline__ int range_start_t(const SkLaunch& a, const int g) {
+  const I C = (I)g * (I)a.total_cost / (I)a.n_grp;
   int si = 0;
   for (int i = 0; i < a.n_sessions; ++i)
-    if (a.s[i].ntiles > 0 && a.s[i].cost_begin <= C) si = i;
+    if (a.s[i].ntiles > 0 && (I)a.s[i].cost_begin <= C) si = i;
   si = __builtin_amdgcn_readfirstlane(si);
   const SkSession& S = a.s[si];
-  const long long m = S.mult;
-  const long long per = m * (S.ntiles + a.piece_cost);
-  const long long r0 = C - S.cost_begin;
-  const long long col = r0 / per;
-  const long long t = (r0 - col * per + m - 1) / m - a.piece_cost;
-  return (int)(S.it_begin + col * S.ntiles + (t > 0 ? t : 0));
+  const I m = (I)S.mult;
+  const I per = m * (I)(S.ntiles + a.piece_cost);
+  const I r0 = C - (I)S.cost_begin;
+  const I col = r0 / per;
+  const int t = (int)((r0 - col * per + m - 1) / m) - a.piece_cost;
+  return (int)(S.it_begin + (int)col * S.ntiles + (t > 0 ? t : 0));
+}
+template <typename I>
+__device__ __forceinline__ int range_start(const SkLaunch& a, const int g) {
+  return g >= a.n_grp ? a.n_iters : range_start_t<I>(a, g);
 }
 
 // Group holding column iteration i: the last g whose range starts at or before it.
+template <typename I>
 __device__ __forceinline__ int grp_of_iter(const SkLaunch& a, const int i) {
   const SkSession& S = a.s[session_of_iter(a, i)];
   const int local = i - S.it_begin;
   const int col = local / S.ntiles;
-  const long long m = S.mult;
-  const long long X = (long long)S.cost_begin + (long long)col * m * (S.ntiles + a.piece_cost) +
-                      m * (a.piece_cost + (local - col * S.ntiles));
-  return (int)(((X + 1) * a.n_grp - 1) / a.total_cost);
+  const I m = (I)S.mult;
+  const I X = (I)S.cost_begin + (I)col * m * (I)(S.ntiles + a.piece_cost) +
+              m * (I)(a.piece_cost + (local - col * S.ntiles));
+  return (int)(((X + 1) * (I)a.n_grp - 1) / (I)a.total_cost);
 }
 
 // Session and unit of a unit index counted over the whole launch.
@@ -258,7 +265,7 @@ __device__ __forceinline__ int fresh_lane() {
   return v;
 }
 
-template <bool REC>
+template <bool REC, typename I>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
@@ -280,8 +287,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   grp = __builtin_amdgcn_readfirstlane(grp);
   mem = __builtin_amdgcn_readfirstlane(mem);
-  const int it_lo = __builtin_amdgcn_readfirstlane(range_start(a, grp));
-  const int it_hi = __builtin_amdgcn_readfirstlane(range_start(a, grp + 1));
+  const int it_lo = __builtin_amdgcn_readfirstlane(range_start<I>(a, grp));
+  const int it_hi = __builtin_amdgcn_readfirstlane(range_start<I>(a, grp + 1));
   const int H = a.n_heads;
   const float c = a.scale_log2;
 
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // piece slot of the column's units: the k-th group of the column writes slot k
-    const int k = grp - grp_of_iter(a, S.it_begin + h * nt);
+    const int k = grp - grp_of_iter<I>(a, S.it_begin + h * nt);
     for (int qt = mem; qt < S.qtiles; qt += GS) {
     const int u = h * S.qtiles + qt;
     if (!q_ok) load_q(S, h, qt);
@@ -841,6 +848,7 @@ static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kC
 // the tail), and writes the normalised output.  kCombSplit workgroups per unit, each
 // owning kCombRows rows; a thread owns 4 columns of kCombPer rows.  Partials are read
 // kCombBatch at a time, all loads in flight before the first is used.
+template <typename I>
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units, int n_wg) {
   // A record written by this launch (one session): the attention read its keys from the
   // source, so the copy into the buffer can wait until now; its loads overlap the loads
@@ -872,7 +880,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   int pieces = 0;
   if (S.ntiles > 0) {
     const int first = S.it_begin + h * S.ntiles;  // the column's first iteration
-    pieces = grp_of_iter(a, first + S.ntiles - 1) - grp_of_iter(a, first) + 1;
+    pieces = grp_of_iter<I>(a, first + S.ntiles - 1) - grp_of_iter<I>(a, first) + 1;
   }
   if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
   const int total = pieces + (has_tail ? 1 : 0);
@@ -944,10 +952,11 @@ size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows) {
 }
 
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
-  if (a.n_sessions == 1 && a.s[0].rec_seg >= 0)
-    launch(attn_sk_kernel<true>, dim3(a.n_wg), dim3(kThreads), stream, a);
-  else
-    launch(attn_sk_kernel<false>, dim3(a.n_wg), dim3(kThreads), stream, a);
+  const bool rec = a.n_sessions == 1 && a.s[0].rec_seg >= 0;
+  if (rec && a.narrow) launch(attn_sk_kernel<true, unsigned>, dim3(a.n_wg), dim3(kThreads), stream, a);
+  else if (rec) launch(attn_sk_kernel<true, long long>, dim3(a.n_wg), dim3(kThreads), stream, a);
+  else if (a.narrow) launch(attn_sk_kernel<false, unsigned>, dim3(a.n_wg), dim3(kThreads), stream, a);
+  else launch(attn_sk_kernel<false, long long>, dim3(a.n_wg), dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 
@@ -959,7 +968,8 @@ hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream
 
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
   const int grid = (a.xcd_map ? 8 * a.xcd_per : total_units) * kCombSplit;
-  launch(combine_sk_kernel, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
+  if (a.narrow) launch(combine_sk_kernel<unsigned>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
+  else launch(combine_sk_kernel<long long>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
   return hipGetLastError();
 }
 

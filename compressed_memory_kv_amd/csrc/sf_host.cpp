@@ -596,6 +596,9 @@ Segs cut_record(const Segs& sg, int64_t row0, int64_t rows, int* rec_seg) {
   return o;
 }
 
+// sf_debug_wide_ranges: head_dim-64 reads take the 64-bit range arithmetic.
+std::atomic<int> g_wide_ranges{0};
+
 sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
                             void* const* out, float scale_log2, hipStream_t st, const RecWrite* rec = nullptr,
                             Arena* arena = nullptr) {
@@ -684,6 +687,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     a.n_iters = (int32_t)iters;
     a.piece_cost = piece_cost;
     a.total_cost = (int32_t)cost;
+    a.narrow = (cost + 1) * NG < ((int64_t)1 << 31) && !g_wide_ranges.load(std::memory_order_relaxed) ? 1 : 0;
     // Group holding tile t of column col of a session, as the attention kernel finds it.
     auto grp_of = [&](const sf::SkSession& s, int64_t col, int64_t t) -> int64_t {
       const int64_t m = s.mult;
@@ -1426,6 +1430,11 @@ sf_status sf_kernel_times_read(sf_buffer* buf, sf_kernel_times* out) {
 sf_status sf_debug_fail_next_launch(sf_buffer* buf) {
   if (!buf) return fail(nullptr, SF_E_ARG, "buffer is NULL");
   buf->fail_next = true;
+  return SF_OK;
+}
+
+sf_status sf_debug_wide_ranges(int32_t on) {
+  g_wide_ranges.store(on != 0 ? 1 : 0, std::memory_order_relaxed);
   return SF_OK;
 }
 
