@@ -257,6 +257,34 @@ __device__ __forceinline__ void seg_tables(const SkSession& S, int* seg_row, int
     }                                                                                     \
   }
 
+// The record of a one-session launch copied into its buffer rows (K then V, 16-byte
+// chunks): share j of n workgroups, kCopyBatch loads in flight per lane before their stores.
+constexpr int kCopyBatch = 16;
+__device__ __forceinline__ void copy_record_share(const SkLaunch& a, const int j, const int n) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const SkSession& S0 = a.s[0];
+  const int n16 = S0.rows * a.n_heads * D * 2 / 16;  // chunks per tensor
+  const size_t dst0 = (size_t)S0.rec_row0 * a.n_heads * D * 2 / 16;
+  const u32x4* __restrict__ sk = reinterpret_cast<const u32x4*>(S0.rec_k);
+  const u32x4* __restrict__ sv = reinterpret_cast<const u32x4*>(S0.rec_v);
+  u32x4* __restrict__ dk = reinterpret_cast<u32x4*>(const_cast<void*>(S0.k)) + dst0;
+  u32x4* __restrict__ dv = reinterpret_cast<u32x4*>(const_cast<void*>(S0.v)) + dst0;
+  const int stride = n * kThreads;
+  for (int i0 = j * kThreads + (int)tid_x(); i0 < 2 * n16; i0 += stride * kCopyBatch) {
+    u32x4 x[kCopyBatch];
+#pragma unroll
+    for (int b = 0; b < kCopyBatch; ++b) {
+      const int i = i0 + b * stride;
+      if (i < 2 * n16) x[b] = __builtin_nontemporal_load(i < n16 ? sk + i : sv + (i - n16));
+    }
+#pragma unroll
+    for (int b = 0; b < kCopyBatch; ++b) {
+      const int i = i0 + b * stride;
+      if (i < 2 * n16) __builtin_nontemporal_store(x[b], i < n16 ? dk + i : dv + (i - n16));
+    }
+  }
+}
+
 // The lane's index, computed where it is used (volatile: never hoisted or kept live
 // across the main loop, where every register counts).
 __device__ __forceinline__ int fresh_lane() {
@@ -277,7 +305,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   int grp, mem;
   if (a.grp_per_xcd > 0) {
     const int per = G >> 3, x = w / per, lw = w - x * per;
-    if (lw >= a.grp_per_xcd * GS) return;  // past the XCD's whole groups: no work
+    const int busy = a.grp_per_xcd * GS;
+    if (lw >= busy) {  // past the XCD's whole groups: no attention work
+      if (REC && a.rec_copy_idle) copy_record_share(a, x * (per - busy) + (lw - busy), 8 * (per - busy));
+      return;
+    }
     grp = x * a.grp_per_xcd + lw / GS;
     mem = lw % GS;
   } else {
@@ -850,10 +882,10 @@ static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kC
 // kCombBatch at a time, all loads in flight before the first is used.
 template <typename I>
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units, int n_wg) {
-  // A record written by this launch (one session): the attention read its keys from the
-  // source, so the copy into the buffer can wait until now; its loads overlap the loads
-  // of the partials below.
-  if (a.n_sessions == 1 && a.s[0].rec_seg >= 0) {
+  // A record written by this launch (one session) and not copied by the attention kernel:
+  // the attention read its keys from the source, so the copy into the buffer can wait
+  // until now; its loads overlap the loads of the partials below.
+  if (a.n_sessions == 1 && a.s[0].rec_seg >= 0 && !a.rec_copy_idle) {
     const SkSession& S0 = a.s[0];
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const size_t n16 = (size_t)S0.rows * a.n_heads * D * 2 / 16;

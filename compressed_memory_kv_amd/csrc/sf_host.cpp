@@ -688,6 +688,8 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     a.piece_cost = piece_cost;
     a.total_cost = (int32_t)cost;
     a.narrow = (cost + 1) * NG < ((int64_t)1 << 31) && !g_wide_ranges.load(std::memory_order_relaxed) ? 1 : 0;
+    // the record copy goes to the attention launch's workgroups past the whole groups, if any
+    a.rec_copy_idle = cnt == 1 && a.s[0].rec_seg >= 0 && iters > 0 && gpx > 0 && per_x > gpx * GS ? 1 : 0;
     // Group holding tile t of column col of a session, as the attention kernel finds it.
     auto grp_of = [&](const sf::SkSession& s, int64_t col, int64_t t) -> int64_t {
       const int64_t m = s.mult;

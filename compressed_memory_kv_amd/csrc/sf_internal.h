@@ -147,6 +147,10 @@ struct SkLaunch {
   // 1 when (T + 1) * NG < 2^31: the range and group formulas then fit 32-bit arithmetic
   // (64-bit divisions cost about 0.7 us at the start of a served read).
   int32_t narrow;
+  // 1: the record of a one-session sf_step launch is copied into its buffer rows by the
+  // attention kernel's workgroups past the XCDs' whole groups (which have no attention
+  // work), while the others read; 0: by combine_sk_kernel.
+  int32_t rec_copy_idle;
   SkSession s[kMaxLaunchSessions];
 };
 // Piece slots per unit a session of capacity C needs (bounded because a group range
