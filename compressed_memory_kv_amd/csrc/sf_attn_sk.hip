@@ -319,8 +319,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   grp = __builtin_amdgcn_readfirstlane(grp);
   mem = __builtin_amdgcn_readfirstlane(mem);
-  const int it_lo = __builtin_amdgcn_readfirstlane(range_start<I>(a, grp));
-  const int it_hi = __builtin_amdgcn_readfirstlane(range_start<I>(a, grp + 1));
+  int it_lo, it_hi, k_first;  // this group's iterations [it_lo, it_hi), its first piece's slot
+  if (a.grp_table) {
+    const int e0 = a.grp_first[grp], e1 = a.grp_first[grp + 1];
+    it_lo = e0 & 0xffffff;
+    k_first = e0 >> 24;
+    it_hi = e1 & 0xffffff;
+  } else {
+    it_lo = range_start<I>(a, grp);
+    it_hi = range_start<I>(a, grp + 1);
+    k_first = -1;
+  }
+  it_lo = __builtin_amdgcn_readfirstlane(it_lo);
+  it_hi = __builtin_amdgcn_readfirstlane(it_hi);
+  k_first = __builtin_amdgcn_readfirstlane(k_first);
   const int H = a.n_heads;
   const float c = a.scale_log2;
 
@@ -451,7 +463,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // piece slot of the column's units: the k-th group of the column writes slot k
-    const int k = grp - grp_of_iter<I>(a, S.it_begin + h * nt);
+    const int k = a.grp_table ? (it == it_lo ? k_first : 0) : grp - grp_of_iter<I>(a, S.it_begin + h * nt);
     for (int qt = mem; qt < S.qtiles; qt += GS) {
     const int u = h * S.qtiles + qt;
     if (!q_ok) load_q(S, h, qt);

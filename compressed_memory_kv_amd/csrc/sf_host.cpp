@@ -696,6 +696,40 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       const int64_t X = (int64_t)s.cost_begin + col * m * (s.ntiles + piece_cost) + m * (piece_cost + t);
       return ((X + 1) * NG - 1) / (cost > 0 ? cost : 1);
     };
+    // First iteration of group g, as the attention kernel finds it: the first tile at or
+    // past cost floor(g*T/NG).
+    auto range_start = [&](int64_t g) -> int64_t {
+      if (g >= NG) return iters;
+      const int64_t C = g * cost / NG;
+      int si = 0;
+      for (int i = 0; i < cnt; ++i)
+        if (a.s[i].ntiles > 0 && a.s[i].cost_begin <= C) si = i;
+      const sf::SkSession& s = a.s[si];
+      const int64_t m = s.mult, per = m * (s.ntiles + piece_cost), r0 = C - s.cost_begin;
+      const int64_t col = r0 / per;
+      const int64_t t = (r0 - col * per + m - 1) / m - piece_cost;
+      return s.it_begin + col * s.ntiles + (t > 0 ? t : 0);
+    };
+    // Group starts and first-piece slots, tabulated (see SkLaunch::grp_table).
+    a.grp_table = 0;
+    if (NG <= sf::kSkGrpTable && iters < ((int64_t)1 << 24) && iters > 0 && !g_wide_ranges.load(std::memory_order_relaxed)) {
+      bool fits = true;
+      for (int64_t g = 0; g <= NG && fits; ++g) {
+        const int64_t it = range_start(g);
+        int64_t k = 0;
+        if (g < NG && it < iters) {
+          int si = 0;
+          for (int i = 0; i < cnt; ++i)
+            if (a.s[i].it_begin <= it) si = i;
+          const sf::SkSession& s = a.s[si];
+          const int64_t col = (it - s.it_begin) / s.ntiles;
+          k = g - grp_of(s, col, 0);
+        }
+        fits = k >= 0 && k < 128;
+        a.grp_first[g] = (int32_t)(it | (k << 24));
+      }
+      a.grp_table = fits ? 1 : 0;
+    }
     // Partial-result slots per unit: the groups its column meets, then one for the tail.
     // A group range holds at least kSkMinRange tiles of a column it starts inside, so this
     // never exceeds the capacity bound the session's own scratch region is sized for.

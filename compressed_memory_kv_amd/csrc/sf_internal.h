@@ -89,6 +89,7 @@ constexpr int kSkMinRange = 8;      // fewest tiles of a column a group range st
 constexpr int kSkWgPerCu = 2;       // persistent workgroups per CU
 constexpr int kSkPieceCost = 7;     // a piece's fixed overhead, in tiles (tuned: 4, 5, 7, 9, 12 measured)
 constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
+constexpr int kSkGrpTable = 384;    // most groups whose ranges the host tabulates
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
   float* out;           // [rows][H][64] fp32
@@ -151,8 +152,17 @@ struct SkLaunch {
   // attention kernel's workgroups past the XCDs' whole groups (which have no attention
   // work), while the others read; 0: by combine_sk_kernel.
   int32_t rec_copy_idle;
+  // grp_table = 1: entry g of grp_first is group g's first iteration (low 24 bits) and
+  // the piece slot of its first piece (high 8 bits), for g <= n_grp (entry n_grp: N), as
+  // the formulas above give them; every later piece of a group starts its column, slot 0.
+  // The host fills it when n_grp <= kSkGrpTable, N < 2^24 and every slot < 128: the
+  // kernel's start-up is bound by the scalar unit, which its CU's 8 waves share.
+  int32_t grp_table;
+  int32_t pad_;
   SkSession s[kMaxLaunchSessions];
+  int32_t grp_first[kSkGrpTable + 1];
 };
+static_assert(sizeof(SkLaunch) <= 4000, "kernel arguments stay under the 4 KB limit");
 // Piece slots per unit a session of capacity C needs (bounded because a group range
 // that starts inside a column holds at least kSkMinRange of its tiles).
 int32_t sk_pieces_per_unit(int64_t capacity_rows);

@@ -303,10 +303,10 @@ const char* sf_last_error(const sf_buffer* buf);
 /* Test hook: the next device launch made through buf fails with SF_E_HIP before launching. */
 sf_status sf_debug_fail_next_launch(sf_buffer* buf);
 
-/* Test hook, process-wide: on != 0 makes every later bf16 head_dim-64 read cut its
- * workgroup ranges in 64-bit arithmetic, the form a launch takes when its cost units times
- * its workgroup groups reach 2^31; 0 restores the 32-bit form for launches that fit it.
- * Both forms give the same ranges, so reads are bit-identical either way.  Returns SF_OK. */
+/* Test hook, process-wide: on != 0 makes every later bf16 head_dim-64 read compute its
+ * workgroup ranges in the kernel in 64-bit arithmetic, the form of launches too large for
+ * the host's range table and for 32-bit arithmetic; 0 restores the usual forms.  All forms
+ * give the same ranges, so reads are bit-identical either way.  Returns SF_OK. */
 sf_status sf_debug_wide_ranges(int32_t on);
 
 /* Kernel timing (tracing).  While enabled on a handle, every kernel the library launches

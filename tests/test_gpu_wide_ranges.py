@@ -1,12 +1,13 @@
-"""The head_dim-64 read with its workgroup ranges cut in 64-bit arithmetic against the same
-read in 32-bit arithmetic and against the oracle.
+"""The head_dim-64 read with its workgroup ranges computed in the kernel in 64-bit arithmetic
+against the same read in its usual form and against the oracle.
 
 Model card "GTA world model: weights and inference code", section "One buffer, no mask": the
 read is one dense softmax over every filled row.  How the bf16 head_dim-64 read splits that
-work over workgroups is the kernel's own affair; it computes the split in 32-bit integers when
-the launch is small enough (cost units times groups below 2^31) and in 64-bit integers
-otherwise.  No launch a test can afford reaches 2^31, so `sf_debug_wide_ranges` forces the
-64-bit form: both forms give the same ranges, so outputs must match bit for bit, and they are
+work over workgroups is the kernel's own affair: the host tabulates each group's first
+iteration when the launch has at most 384 groups, and the kernel otherwise computes them, in
+32-bit integers when cost units times groups stay below 2^31 and in 64-bit integers beyond.
+Test launches mostly stay in the table, so `sf_debug_wide_ranges` forces the computed
+64-bit form: all forms give the same ranges, so outputs must match bit for bit, and they are
 checked against the oracle as well.
 """
 import numpy as np
