@@ -36,7 +36,7 @@ EXPORTED = (
     "sf_buffer_destroy", "sf_write_record", "sf_evict", "sf_attend", "sf_step", "sf_query", "sf_plan",
     "sf_status_str", "sf_last_error", "sf_debug_fail_next_launch", "sf_profile_enable", "sf_kernel_times_read",
     "sf_record_slot", "sf_commit_record", "sf_state_bytes", "sf_state_export", "sf_state_import", "sf_rope_rows",
-    "sf_set_recency_bias", "sf_attend_static_scratch", "sf_debug_lds_copy", "sf_debug_wide_ranges",
+    "sf_set_recency_bias", "sf_attend_static_scratch", "sf_debug_lds_copy", "sf_debug_range_form",
 )
 (SF_K_FILL, SF_K_WRITE, SF_K_EVICT, SF_K_ATTEND, SF_K_COMBINE, SF_K_TAIL, SF_K_SINK, SF_K_ROPE, SF_K_BIAS,
  SF_K_KINDS) = range(10)
@@ -84,7 +84,7 @@ _sig = {
     "sf_last_error": (ctypes.c_char_p, [_P]),
     "sf_debug_fail_next_launch": (ctypes.c_int, [_P]),
     "sf_debug_lds_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
-    "sf_debug_wide_ranges": (ctypes.c_int, [ctypes.c_int32]),
+    "sf_debug_range_form": (ctypes.c_int, [ctypes.c_int32]),
     "sf_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "sf_kernel_times_read": (ctypes.c_int, [_P, ctypes.POINTER(sf_kernel_times)]),
     "sf_record_slot": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
@@ -256,8 +256,8 @@ def sf_debug_fail_next_launch(handle: int) -> None:
     _check(_lib.sf_debug_fail_next_launch(handle), handle)
 
 
-def sf_debug_wide_ranges(on: bool) -> None:
-    _check(_lib.sf_debug_wide_ranges(1 if on else 0))
+def sf_debug_range_form(form: int) -> None:
+    _check(_lib.sf_debug_range_form(int(form)))
 
 
 def sf_debug_lds_copy(dst, src, nbytes: int, stream=None) -> None:

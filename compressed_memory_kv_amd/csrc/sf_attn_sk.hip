@@ -169,6 +169,18 @@ __device__ __forceinline__ int grp_of_iter(const SkLaunch& a, const int i) {
   return (int)(((X + 1) * (I)a.n_grp - 1) / (I)a.total_cost);
 }
 
+// Group holding column iteration i from the host's table (SkLaunch::grp_table): the last g
+// whose range starts at or before it.
+__device__ __forceinline__ int grp_of_tab(const SkLaunch& a, const int i) {
+  int lo = 0, hi = a.n_grp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((a.grp_first[mid] & 0xffffff) <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Session and unit of a unit index counted over the whole launch.
 __device__ __forceinline__ void decode_unit(const SkLaunch& a, int ug, int& si, int& u) {
   int s = 0, base = 0, acc = 0;
@@ -924,7 +936,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   int pieces = 0;
   if (S.ntiles > 0) {
     const int first = S.it_begin + h * S.ntiles;  // the column's first iteration
-    pieces = grp_of_iter<I>(a, first + S.ntiles - 1) - grp_of_iter<I>(a, first) + 1;
+    pieces = a.grp_table ? grp_of_tab(a, first + S.ntiles - 1) - grp_of_tab(a, first) + 1
+                         : grp_of_iter<I>(a, first + S.ntiles - 1) - grp_of_iter<I>(a, first) + 1;
   }
   if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
   const int total = pieces + (has_tail ? 1 : 0);

@@ -22,6 +22,7 @@
 //   "Files", "Credits"          the optional recency bias on summary keys, by age.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -596,8 +597,9 @@ Segs cut_record(const Segs& sg, int64_t row0, int64_t rows, int* rec_seg) {
   return o;
 }
 
-// sf_debug_wide_ranges: head_dim-64 reads take the 64-bit range arithmetic.
-std::atomic<int> g_wide_ranges{0};
+// sf_debug_range_form: 0 the library's choice, 1 the kernel's formula (32-bit where it
+// fits), 2 the kernel's formula in 64-bit arithmetic.
+std::atomic<int> g_range_form{0};
 
 sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, const void* const* q,
                             void* const* out, float scale_log2, hipStream_t st, const RecWrite* rec = nullptr,
@@ -687,20 +689,14 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
     a.n_iters = (int32_t)iters;
     a.piece_cost = piece_cost;
     a.total_cost = (int32_t)cost;
-    a.narrow = (cost + 1) * NG < ((int64_t)1 << 31) && !g_wide_ranges.load(std::memory_order_relaxed) ? 1 : 0;
+    const int form = g_range_form.load(std::memory_order_relaxed);
+    a.narrow = (cost + 1) * NG < ((int64_t)1 << 31) && form != 2 ? 1 : 0;
     // the record copy goes to the attention launch's workgroups past the whole groups, if any
     a.rec_copy_idle = cnt == 1 && a.s[0].rec_seg >= 0 && iters > 0 && gpx > 0 && per_x > gpx * GS ? 1 : 0;
-    // Group holding tile t of column col of a session, as the attention kernel finds it.
-    auto grp_of = [&](const sf::SkSession& s, int64_t col, int64_t t) -> int64_t {
-      const int64_t m = s.mult;
-      const int64_t X = (int64_t)s.cost_begin + col * m * (s.ntiles + piece_cost) + m * (piece_cost + t);
-      return ((X + 1) * NG - 1) / (cost > 0 ? cost : 1);
-    };
-    // First iteration of group g, as the attention kernel finds it: the first tile at or
-    // past cost floor(g*T/NG).
-    auto range_start = [&](int64_t g) -> int64_t {
-      if (g >= NG) return iters;
-      const int64_t C = g * cost / NG;
+    // First column iteration at or past cost C: the first tile whose cost, mult *
+    // (piece_cost + t) from its column's start, is at least C.
+    auto iter_at_cost = [&](int64_t C) -> int64_t {
+      if (C >= cost) return iters;
       int si = 0;
       for (int i = 0; i < cnt; ++i)
         if (a.s[i].ntiles > 0 && a.s[i].cost_begin <= C) si = i;
@@ -710,40 +706,93 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       const int64_t t = (r0 - col * per + m - 1) / m - piece_cost;
       return s.it_begin + col * s.ntiles + (t > 0 ? t : 0);
     };
-    // Group starts and first-piece slots, tabulated (see SkLaunch::grp_table).
+    // Group g takes the iterations [gstart[g], gstart[g+1]).  The kernel's own formula cuts
+    // at costs floor(g*T/NG); the host table may cut at costs weighted per group instead:
+    // of the two workgroups a CU holds, the one dispatched first issues faster (measured
+    // 0.98 against 1.09 us per tile at the served shape), and the remap puts whole groups on
+    // one side, so groups of first-dispatched workgroups get more cost units.
+    std::vector<int64_t> gstart((size_t)NG + 1);
+    auto cut = [&](bool weighted) {
+      std::vector<double> w((size_t)NG, 1.0);
+      if (weighted) {
+        for (int64_t g = 0; g < NG; ++g) {
+          double sum = 0.0;
+          for (int64_t j = 0; j < GS; ++j) {
+            const int64_t lw = (g % gpx) * GS + j;  // logical workgroup within the XCD
+            sum += lw < per_x / 2 ? 1.0 + sf::kSkDispatchSkew / 2 : 1.0 - sf::kSkDispatchSkew / 2;
+          }
+          w[(size_t)g] = sum / (double)GS;
+        }
+      }
+      double total = 0.0;
+      for (double x : w) total += x;
+      double acc = 0.0;
+      for (int64_t g = 0; g < NG; ++g) {
+        const int64_t C = weighted ? (int64_t)((double)cost * (acc / total)) : g * cost / NG;
+        gstart[(size_t)g] = iter_at_cost(C);
+        acc += w[(size_t)g];
+      }
+      gstart[(size_t)NG] = iters;
+    };
+    // Group holding iteration i: the last g whose range starts at or before it.
+    auto grp_at = [&](int64_t i) -> int64_t {
+      return (int64_t)(std::upper_bound(gstart.begin(), gstart.begin() + NG, i) - gstart.begin()) - 1;
+    };
+    // Partial-result slots per unit: the groups its column meets, then one for the tail.
+    // With the formula's cut a group range holds at least kSkMinRange tiles of a column it
+    // starts inside, so this never exceeds the capacity bound the session's own scratch
+    // region is sized for; a weighted cut that would is dropped for the formula's.
+    auto slots_fit = [&]() {
+      for (int i = 0; i < cnt; ++i) {
+        sf::SkSession& s = a.s[i];
+        int64_t pieces = 0;
+        for (int64_t h = 0; s.ntiles > 0 && h < H; ++h) {
+          const int64_t c0 = s.it_begin + h * s.ntiles;
+          const int64_t p = grp_at(c0 + s.ntiles - 1) - grp_at(c0) + 1;
+          pieces = p > pieces ? p : pieces;
+        }
+        s.ppu = (int32_t)(pieces + 1);
+        if (s.ppu > sf::sk_pieces_per_unit(bufs[first + i]->geo.C)) return false;
+      }
+      return true;
+    };
+    const bool table = NG <= sf::kSkGrpTable && iters < ((int64_t)1 << 24) && iters > 0 && form == 0;
+    const bool skew = table && gpx > 0 && G == (int64_t)sf::kSkWgPerCu * device_cu_count() && sf::kSkWgPerCu == 2;
+    cut(skew);
+    bool fit = slots_fit();
+    if (!fit && skew) {
+      cut(false);
+      fit = slots_fit();
+    }
+    if (!fit) return fail(b0, SF_E_UNSUPPORTED, "internal: stream-K partial slots exceed the session's scratch bound");
+    // Group starts and first-piece slots, tabulated (see SkLaunch::grp_table).  Without the
+    // table the kernel computes the formula's cut itself, which gstart then equals.
     a.grp_table = 0;
-    if (NG <= sf::kSkGrpTable && iters < ((int64_t)1 << 24) && iters > 0 && !g_wide_ranges.load(std::memory_order_relaxed)) {
+    if (table) {
       bool fits = true;
       for (int64_t g = 0; g <= NG && fits; ++g) {
-        const int64_t it = range_start(g);
+        const int64_t it = gstart[(size_t)g];
         int64_t k = 0;
         if (g < NG && it < iters) {
           int si = 0;
           for (int i = 0; i < cnt; ++i)
             if (a.s[i].it_begin <= it) si = i;
           const sf::SkSession& s = a.s[si];
-          const int64_t col = (it - s.it_begin) / s.ntiles;
-          k = g - grp_of(s, col, 0);
+          const int64_t c0 = s.it_begin + (it - s.it_begin) / s.ntiles * s.ntiles;
+          k = g - grp_at(c0);
         }
         fits = k >= 0 && k < 128;
         a.grp_first[g] = (int32_t)(it | (k << 24));
       }
       a.grp_table = fits ? 1 : 0;
+      if (!fits && skew) {
+        cut(false);  // the kernel computes the formula's cut
+        if (!slots_fit()) return fail(b0, SF_E_UNSUPPORTED, "internal: stream-K partial slots exceed the session's scratch bound");
+      }
     }
-    // Partial-result slots per unit: the groups its column meets, then one for the tail.
-    // A group range holds at least kSkMinRange tiles of a column it starts inside, so this
-    // never exceeds the capacity bound the session's own scratch region is sized for.
     for (int i = 0; i < cnt; ++i) {
       sf_buffer* b = bufs[first + i];
       sf::SkSession& s = a.s[i];
-      int64_t pieces = 0;
-      for (int64_t h = 0; s.ntiles > 0 && h < H; ++h) {
-        const int64_t p = grp_of(s, h, s.ntiles - 1) - grp_of(s, h, 0) + 1;
-        pieces = p > pieces ? p : pieces;
-      }
-      s.ppu = (int32_t)(pieces + 1);
-      if (s.ppu > sf::sk_pieces_per_unit(b->geo.C))
-        return fail(b0, SF_E_UNSUPPORTED, "internal: stream-K partial slots exceed the session's scratch bound");
       const int64_t units = (int64_t)H * s.qtiles;
       const size_t bytes = (size_t)units * s.ppu * sf::kSkRows * (64 + 2) * sizeof(float);
       char* base = b->mem + b->geo.scratch_off;
@@ -768,7 +817,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
         const int64_t units = (int64_t)H * s.qtiles;
         for (int64_t u = 0; u < units; ++u) {
           int x = x_prev;
-          if (s.ntiles > 0) x = (int)(grp_of(s, u / s.qtiles, 0) / gpx);
+          if (s.ntiles > 0) x = (int)(grp_at(s.it_begin + u / s.qtiles * s.ntiles) / gpx);
           x = x < x_prev ? x_prev : (x > 7 ? 7 : x);
           x_prev = x;
           ++count[x];
@@ -1469,8 +1518,9 @@ sf_status sf_debug_fail_next_launch(sf_buffer* buf) {
   return SF_OK;
 }
 
-sf_status sf_debug_wide_ranges(int32_t on) {
-  g_wide_ranges.store(on != 0 ? 1 : 0, std::memory_order_relaxed);
+sf_status sf_debug_range_form(int32_t form) {
+  if (form < 0 || form > 2) return fail(nullptr, SF_E_ARG, "sf_debug_range_form: form must be 0, 1 or 2");
+  g_range_form.store(form, std::memory_order_relaxed);
   return SF_OK;
 }
 

@@ -90,6 +90,11 @@ constexpr int kSkWgPerCu = 2;       // persistent workgroups per CU
 constexpr int kSkPieceCost = 7;     // a piece's fixed overhead, in tiles (tuned: 4, 5, 7, 9, 12 measured)
 constexpr int kRecSlot = SF_MAX_SEGMENTS - 1;  // segment slot of a record read from its source
 constexpr int kSkGrpTable = 384;    // most groups whose ranges the host tabulates
+// Cost weight of a workgroup dispatched first on its CU over one dispatched second, minus
+// one: the weighted cut the host tabulates gives the first 1 + skew/2, the second 1 - skew/2
+// (measured at the served shape: 0 -> 42.6 us, 0.06 / 0.10 / 0.14 -> 43.0 / 42.2 / 41.9,
+// 0.20 to 0.45 -> 40.5 to 41.4; the batched read slows past 0.20).
+constexpr double kSkDispatchSkew = 0.20;
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
   float* out;           // [rows][H][64] fp32

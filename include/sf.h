@@ -303,11 +303,14 @@ const char* sf_last_error(const sf_buffer* buf);
 /* Test hook: the next device launch made through buf fails with SF_E_HIP before launching. */
 sf_status sf_debug_fail_next_launch(sf_buffer* buf);
 
-/* Test hook, process-wide: on != 0 makes every later bf16 head_dim-64 read compute its
- * workgroup ranges in the kernel in 64-bit arithmetic, the form of launches too large for
- * the host's range table and for 32-bit arithmetic; 0 restores the usual forms.  All forms
- * give the same ranges, so reads are bit-identical either way.  Returns SF_OK. */
-sf_status sf_debug_wide_ranges(int32_t on);
+/* Test hook, process-wide: how every later bf16 head_dim-64 read cuts its work into
+ * workgroup ranges.  form 0: the library's choice (a table of ranges made by the host,
+ * weighted by how fast each workgroup group runs, when the launch has at most 384 groups;
+ * else computed by the kernel); 1: computed by the kernel from the unweighted formula, in
+ * 32-bit arithmetic where it fits; 2: the same in 64-bit arithmetic, the form of the
+ * largest launches.  Forms 1 and 2 give the same ranges, so their reads are bit-identical;
+ * form 0's ranges differ, so its reads differ by rounding.  SF_E_ARG for another form. */
+sf_status sf_debug_range_form(int32_t form);
 
 /* Kernel timing (tracing).  While enabled on a handle, every kernel the library launches
  * for it is given two HIP events that its dispatch stamps with its own start and end (on
