@@ -418,6 +418,16 @@ void attn_bf16_kernel(const AttnLaunch a) {
   store_bias(st_a, bra);
   __syncthreads();
   for (int tile = t0; tile < t1; tile += 2) {
+    // Issue priority from progress through the unit's tiles, 3 in the first quarter down to
+    // 0 in the last: the workgroups sharing a CU then keep level (the arbiter otherwise
+    // favours the one dispatched first, and the last one to finish sets the launch's time).
+    {
+      const int q = (4 * (tile - t0)) / (t1 - t0);
+      if (q <= 0) __builtin_amdgcn_s_setprio(3);
+      else if (q == 1) __builtin_amdgcn_s_setprio(2);
+      else if (q == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     if (tile + 1 < t1) dma_tile(tile + 1, st_b, brb);
     if (wave_on) compute_tile(tile, st_a);
     if (tile + 1 < t1) store_bias(st_b, brb);
