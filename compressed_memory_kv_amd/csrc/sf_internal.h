@@ -93,7 +93,8 @@ constexpr int kSkGrpTable = 384;    // most groups whose ranges the host tabulat
 // Cost weight of a workgroup dispatched first on its CU over one dispatched second, minus
 // one: the weighted cut the host tabulates gives the first 1 + skew/2, the second 1 - skew/2
 // (measured at the served shape: 0 -> 42.6 us, 0.06 / 0.10 / 0.14 -> 43.0 / 42.2 / 41.9,
-// 0.20 to 0.45 -> 40.5 to 41.4; the batched read slows past 0.20).
+// 0.20 to 0.45 -> 40.5 to 41.4); one-session launches only (a batch of sessions measured
+// slower weighted).
 constexpr double kSkDispatchSkew = 0.20;
 struct SkSession {
   const void* q;        // [rows][H][64] bf16
