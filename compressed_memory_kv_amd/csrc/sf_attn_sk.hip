@@ -32,7 +32,9 @@
 //   combine_sk_kernel: merges the partials of every unit that has more than one.
 // sf_step launches fold the record write in: the attention kernels read the new
 // record's keys from the caller's K/V (segment slot kRecSlot, after the buffer's
-// keys) and combine_sk_kernel copies the record into the buffer.
+// keys) and copy the record into the buffer meanwhile with the workgroups past the XCDs'
+// whole groups, which have no attention work (combine_sk_kernel makes the copy when a
+// launch has none).
 //
 // Inside a workgroup of attn_sk_kernel.  Four waves = two key streams x two waves;
 // the piece's tiles are cut into two contiguous halves, one per stream.  The two

@@ -105,7 +105,7 @@ struct SkSession {
   float* part_ml;       // [units][ppu][kSkRows][2] (reference max in log2 units, row sum)
   // A record written by this launch (sf_step): its K/V are read from rec_k / rec_v
   // (segment slot kRecSlot, rows counted from the record's first row, keys last) while
-  // combine_sk_kernel copies them into the buffer at row rec_row0.  rec_seg = kRecSlot
+  // they are copied into the buffer at row rec_row0 (see SkLaunch::rec_copy_idle).  rec_seg = kRecSlot
   // when present, -1 otherwise.  Unused segment slots have length 0.
   const void* rec_k;    // [rows][H][64] bf16
   const void* rec_v;
