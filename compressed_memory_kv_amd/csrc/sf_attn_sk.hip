@@ -92,11 +92,10 @@ constexpr int STAGE_ALL = kStreams * STAGE;           // one stage of every stre
 constexpr int DMA_ROWS = 8;                           // rows one wave-wide 1 KB transfer covers
 constexpr int DMA_PER_WAVE = BN / DMA_ROWS / 2;       // transfers per wave per tensor per tile (4)
 constexpr float kOverflowSum = 0x1p40f;               // a lane quarter sum above this asks for exact maxima
-// Stream merge buffer: stream 1's 2 waves x 64 lanes x (64 O + 2 m + 2 l) floats, the
-// slot of wave hw in stage array a (hw = 0) or b (hw = 1).
-constexpr int MERGE_FLOATS = 68;
-constexpr int MERGE_SLOT = 64 * MERGE_FLOATS * 4;
-static_assert(MERGE_SLOT <= STAGE_ALL, "a merge slot fits in one stage array");
+// Stream merge: the wave of stream s with query rows hw leaves the other stream the d block
+// that one finishes, in stage array hw at slot s (64 lanes x XCHG_FLOATS floats each).
+constexpr int XCHG_FLOATS = 36;  // per lane: one d block of both query blocks (32), references, sums
+static_assert(kStreams * 64 * XCHG_FLOATS * 4 <= STAGE_ALL, "both streams' exchange slots fit in one stage array");
 static_assert(BN == 64, "a tile is two 32-key MFMA blocks");
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
@@ -673,94 +672,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
-    // ---- merge the two streams (stream 0 collects), then write
+    // ---- merge the two streams: stream s finishes d block s (head dims 32s .. 32s+31) of
+    // both query blocks.  Each wave hands the wave of the other stream with the same query
+    // rows the d block that one finishes, with its references and sums.
     const int mlane = fresh_lane();
-    auto merge_slot = [&](const int sl) -> float* {
-      return reinterpret_cast<float*>(sl == 0 ? st_a : st_b) + mlane * MERGE_FLOATS;
+    auto xslot = [&](const int sm) -> float* {  // slot of stream sm's wave of this hw
+      return reinterpret_cast<float*>(hw == 0 ? st_a : st_b) + (sm * 64 + mlane) * XCHG_FLOATS;
     };
-    if (stream > 0 && wave_on) {
-      float* dst = merge_slot((stream - 1) * 2 + hw);
+    if (wave_on) {
+      float* dst = xslot(stream);
+      const f32x16& g0 = stream == 0 ? o10 : o00;
+      const f32x16& g1 = stream == 0 ? o11 : o01;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        *reinterpret_cast<float4*>(dst + 0 * 16 + r) = make_float4(o00[r], o00[r + 1], o00[r + 2], o00[r + 3]);
-        *reinterpret_cast<float4*>(dst + 1 * 16 + r) = make_float4(o01[r], o01[r + 1], o01[r + 2], o01[r + 3]);
-        *reinterpret_cast<float4*>(dst + 2 * 16 + r) = make_float4(o10[r], o10[r + 1], o10[r + 2], o10[r + 3]);
-        *reinterpret_cast<float4*>(dst + 3 * 16 + r) = make_float4(o11[r], o11[r + 1], o11[r + 2], o11[r + 3]);
+        *reinterpret_cast<float4*>(dst + r) = make_float4(g0[r], g0[r + 1], g0[r + 2], g0[r + 3]);
+        *reinterpret_cast<float4*>(dst + 16 + r) = make_float4(g1[r], g1[r + 1], g1[r + 2], g1[r + 3]);
       }
-      *reinterpret_cast<float4*>(dst + 64) = make_float4(mref0, mref1, lsum0, lsum1);
+      *reinterpret_cast<float4*>(dst + 32) = make_float4(mref0, mref1, lsum0, lsum1);
     }
     __syncthreads();
-    if (stream == 0 && wave_on) {
-      float mx0 = mref0, mx1 = mref1;
-#pragma unroll
-      for (int s2 = 0; s2 < kStreams - 1; ++s2) {
-        const float4 ml = *reinterpret_cast<const float4*>(merge_slot(s2 * 2 + hw) + 64);
-        mx0 = fmaxf(mx0, ml.x);
-        mx1 = fmaxf(mx1, ml.y);
-      }
+    if (wave_on) {
+      const float* src = xslot(1 - stream);
+      const float4 ml = *reinterpret_cast<const float4*>(src + 32);
       // a stream without tiles has reference -inf and contributes nothing
-      const float f00 = __builtin_amdgcn_exp2f(mref0 - mx0), f01 = __builtin_amdgcn_exp2f(mref1 - mx1);
-      float l0 = lsum0 * f00, l1 = lsum1 * f01;
-      o00 *= f00;
-      o10 *= f00;
-      o01 *= f01;
-      o11 *= f01;
-#pragma unroll 1
-      for (int s2 = 0; s2 < kStreams - 1; ++s2) {  // one stream at a time keeps the live set small
-        const float* src = merge_slot(s2 * 2 + hw);
-        const float4 ml = *reinterpret_cast<const float4*>(src + 64);
-        const float f0 = __builtin_amdgcn_exp2f(ml.x - mx0);
-        const float f1 = __builtin_amdgcn_exp2f(ml.y - mx1);
-        l0 += ml.z * f0;
-        l1 += ml.w * f1;
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float4 x00 = *reinterpret_cast<const float4*>(src + 0 * 16 + r);
-          const float4 x01 = *reinterpret_cast<const float4*>(src + 1 * 16 + r);
-          const float4 x10 = *reinterpret_cast<const float4*>(src + 2 * 16 + r);
-          const float4 x11 = *reinterpret_cast<const float4*>(src + 3 * 16 + r);
-          o00[r] += f0 * x00.x; o00[r + 1] += f0 * x00.y; o00[r + 2] += f0 * x00.z; o00[r + 3] += f0 * x00.w;
-          o01[r] += f1 * x01.x; o01[r + 1] += f1 * x01.y; o01[r + 2] += f1 * x01.z; o01[r + 3] += f1 * x01.w;
-          o10[r] += f0 * x10.x; o10[r + 1] += f0 * x10.y; o10[r + 2] += f0 * x10.z; o10[r + 3] += f0 * x10.w;
-          o11[r] += f1 * x11.x; o11[r + 1] += f1 * x11.y; o11[r + 2] += f1 * x11.z; o11[r + 3] += f1 * x11.w;
-        }
-      }
+      const float mx0 = fmaxf(mref0, ml.x), mx1 = fmaxf(mref1, ml.y);
+      const float fa0 = __builtin_amdgcn_exp2f(mref0 - mx0), fa1 = __builtin_amdgcn_exp2f(mref1 - mx1);
+      const float fb0 = __builtin_amdgcn_exp2f(ml.x - mx0), fb1 = __builtin_amdgcn_exp2f(ml.y - mx1);
+      const float l0 = lsum0 * fa0 + ml.z * fb0, l1 = lsum1 * fa1 + ml.w * fb1;
       const float lt0 = l0 + xor32(l0), lt1 = l1 + xor32(l1);
       const bool has_tail = (S.n_keys & (BN - 1)) != 0;
       const bool whole = tile0 == 0 && tile1 == nt && !has_tail;
       const int el32 = mlane & 31, eg = mlane >> 5;
+      const int dofs = 32 * stream;  // this stream's d block
+      auto finish = [&](const f32x16& a0, const f32x16& a1) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int row = qrow0 + 32 * qb + el32;
-        if (row >= S.rows) continue;
-        const f32x16& oa = qb == 0 ? o00 : o01;
-        const f32x16& ob = qb == 0 ? o10 : o11;
-        const float lt = qb == 0 ? lt0 : lt1;
-        const float mx = qb == 0 ? mx0 : mx1;
-        if (whole) {
-          const float inv = 1.0f / lt;
-          float* op = S.out + row * row_stride + h * D;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            *reinterpret_cast<float4*>(op + 8 * q4 + 4 * eg) =
-                make_float4(oa[4 * q4] * inv, oa[4 * q4 + 1] * inv, oa[4 * q4 + 2] * inv, oa[4 * q4 + 3] * inv);
-            *reinterpret_cast<float4*>(op + 32 + 8 * q4 + 4 * eg) =
-                make_float4(ob[4 * q4] * inv, ob[4 * q4 + 1] * inv, ob[4 * q4 + 2] * inv, ob[4 * q4 + 3] * inv);
-          }
-        } else {
-          const size_t slot = (size_t)u * S.ppu + k;
-          const int rin = row - qt * kSkRows;
-          float* po = S.part_o + (slot * kSkRows + rin) * D;
+        for (int qb = 0; qb < 2; ++qb) {
+          const int row = qrow0 + 32 * qb + el32;
+          if (row >= S.rows) continue;
+          const f32x16& oa = qb == 0 ? a0 : a1;
+          const float fa = qb == 0 ? fa0 : fa1, fb = qb == 0 ? fb0 : fb1;
+          const float lt = qb == 0 ? lt0 : lt1;
+          const float mx = qb == 0 ? mx0 : mx1;
+          const float* xs = src + 16 * qb;
+          const float sc = whole ? 1.0f / lt : 1.0f;
+          float* dp = whole ? S.out + row * row_stride + h * D + dofs
+                            : S.part_o + (((size_t)u * S.ppu + k) * kSkRows + (row - qt * kSkRows)) * D + dofs;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            *reinterpret_cast<float4*>(po + 8 * q4 + 4 * eg) =
-                make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
-            *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * eg) =
-                make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
+            const float4 x = *reinterpret_cast<const float4*>(xs + 4 * q4);
+            *reinterpret_cast<float4*>(dp + 8 * q4 + 4 * eg) =
+                make_float4((oa[4 * q4] * fa + x.x * fb) * sc, (oa[4 * q4 + 1] * fa + x.y * fb) * sc,
+                            (oa[4 * q4 + 2] * fa + x.z * fb) * sc, (oa[4 * q4 + 3] * fa + x.w * fb) * sc);
           }
-          if (eg == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mx, lt);
+          if (!whole && stream == 0 && eg == 0)
+            *reinterpret_cast<float2*>(S.part_ml + (((size_t)u * S.ppu + k) * kSkRows + (row - qt * kSkRows)) * 2) =
+                make_float2(mx, lt);
         }
-      }
+      };
+      if (stream == 0) finish(o00, o01);
+      else finish(o10, o11);
     }
     __syncthreads();  // the merge buffer overlays the stages of the next piece
     }
