@@ -424,7 +424,7 @@ def batched_leg(sf, sf_inputs, torch, steps, warmup=2):
         "keys_per_block": sum(keys),
         "flop_per_block": flop_block,
         "ms_per_step": round(ms / steps, 4),
-        "tflops": round(flop_block * nb / (ms * 1e-3) / 1e12, 2),
+        "tflops": round(flop_block * nb / (ms / steps * 1e-3) / 1e12, 2),
         "attn_kernel": "attn_sk_kernel<false> (stream-K over all 8 sessions) + attn_tail_kernel + combine_sk_kernel",
         "attn_avg_us": round(avg("attend") * 1e3, 3),
         "attn_tflops": round(flop_block / (avg("attend") * 1e-3) / 1e12, 2),
