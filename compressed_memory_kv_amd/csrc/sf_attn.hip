@@ -188,6 +188,10 @@ void attn_bf16_kernel(const AttnLaunch a) {
   constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;             // MFMA k-steps over head_dim
   constexpr int DBLK = D / 32;               // 32-row blocks of O^T
+  constexpr int NQK = KSTEPS * KB;           // MFMAs of S^T per tile
+  constexpr int NPV = DBLK * 2 * KB;         // MFMAs of O^T per tile
+  constexpr int KPF = D == 128 && BIAS ? 2 : 4;  // K operands read ahead of their MFMA (fits the VGPR budget)
+  constexpr int VPF = 2;                     // V^T operands read ahead of their MFMA
   static_assert(BN <= kThreads, "one thread stages each key's bias");
   // Two stages, each in an array of its own: the compiler then knows that transfers into
   // one stage never alias the operand reads of the other (one array would make it wait for
@@ -322,13 +326,26 @@ void attn_bf16_kernel(const AttnLaunch a) {
     for (int b = 0; b < KB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sb[b][r] = 0.0f;
+    // K operands KPF ahead of their MFMA, so an operand's LDS latency overlaps the MFMAs
+    // before it (operand i = k-step i / KB of block i % KB).
+    {
+      bf16x8 ka[NQK];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+      for (int i = 0; i < KPF; ++i)
+        ka[i] = *reinterpret_cast<const bf16x8*>(st + kaddr[i / KB] + 32 * (i % KB) * T::ROW);
 #pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        const bf16x8 ab = *reinterpret_cast<const bf16x8*>(st + kaddr[kk] + 32 * b * T::ROW);
-        sb[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, qreg[kk], sb[b], 0, 0, 0);
+      for (int i = 0; i < NQK; ++i) {
+        if (i + KPF < NQK)
+          ka[i + KPF] = *reinterpret_cast<const bf16x8*>(st + kaddr[(i + KPF) / KB] + 32 * ((i + KPF) % KB) * T::ROW);
+        sb[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qreg[i / KB], sb[i % KB], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+      for (int i = 0; i < NQK - KPF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
     }
     // ---- keys past the end of this unit's range (ragged last tile) score -inf
     if (tile * BN + BN > key_hi) {
@@ -397,16 +414,30 @@ void attn_bf16_kernel(const AttnLaunch a) {
     lsum += ts;
     // ---- O^T += V^T . P^T ; k-step j covers S^T registers 8*(j&1).. of block j>>1,
     // i.e. keys 32*(j>>1) + 16*(j&1) + {4g..4g+3} then {8+4g..8+4g+3}.
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-      for (int j = 0; j < 2 * KB; ++j) {
+    // V^T operands VPF ahead of their MFMA (operand i = d block i / (2 KB), k-step i % (2 KB)).
+    {
+      auto vload = [&](const int i) {
+        const int db = i / (2 * KB), j = i % (2 * KB);
         const int roff = (32 * (j >> 1) + 16 * (j & 1)) * T::ROW;
         const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff));
         const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vaddr[db] + roff + 8 * T::ROW));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j], o[db], 0, 0, 0);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 av[NPV];
+#pragma unroll
+      for (int i = 0; i < VPF; ++i) av[i] = vload(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + VPF < NPV) av[i + VPF] = vload(i + VPF);
+        o[i / (2 * KB)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pb[i % (2 * KB)], o[i / (2 * KB)], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+      for (int i = 0; i < NPV - VPF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, VPF, 0);
     }
   };
 
