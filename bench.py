@@ -68,6 +68,8 @@ def parse():
                     help="skip the long-horizon leg (24 heads of 128, 46,688 keys per read)")
     ap.add_argument("--no-batched-leg", action="store_true",
                     help="skip the batched leg (8 sessions at fill levels 0..31, one sf_attend per block)")
+    ap.add_argument("--no-heads-leg", action="store_true",
+                    help="skip the head-count leg (2/4/8 heads: one GPU's share under head sharding; 20 heads)")
     ap.add_argument("--long-steps", type=int, default=4, help="timed frames of the long-horizon leg")
     return ap.parse_args()
 
@@ -279,6 +281,30 @@ def bias_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup):
         "bias_rows_launches": kt["bias"][1],
         "attend_launches": kt["attend"][1],
     }
+
+
+def heads_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, heads=(2, 4, 8, 20)):
+    """The served rollout (28 blocks, 6,528 keys per read) with other head counts: 2, 4 and 8
+    heads are one GPU's share of the 16 heads under 8-, 4- and 2-way head sharding (every head's
+    memory, writes and read stay on its GPU); 20 heads of 64 is the width the model card gives
+    its model.  Per head count: frames/s of the share and the stream-K read's durations."""
+    R, D = wl["hw"] + wl["x"], wl["head_dim"]
+    res = {}
+    for H in heads:
+        ms, kt = run_leg(sf, sf_inputs, torch, dict(wl, n_heads=H), steps, warmup, sink_gap=sink_gap)
+        avg = lambda kind: kt[kind][0] / max(kt[kind][1], 1)
+        flop = 4.0 * R * 6528 * H * D
+        call = (kt["attend"][0] + kt["tail"][0] + kt["combine"][0]) / max(kt["attend"][1], 1)
+        res[str(H)] = {
+            "frames_per_s": round(steps / (ms * 1e-3), 2),
+            "attn_avg_us": round(avg("attend") * 1e3, 3),
+            "attn_tflops": round(flop / (avg("attend") * 1e-3) / 1e12, 2),
+            "attn_frac_mfma": round(flop / (avg("attend") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attend_call_us": round(call * 1e3, 3),
+            "attend_call_frac_mfma": round(flop / (call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+    return {"workload": "served rollout with H heads of 64 (2/4/8: one GPU's share under 8/4/2-way head "
+                        "sharding; 20: the model card's width); step = 28 x sf_step", "by_heads": res}
 
 
 def long_leg(sf, sf_inputs, torch, steps, warmup=1):
@@ -598,6 +624,8 @@ def main():
         result["bias_leg"] = bias_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_batched_leg:
         result["batched_leg"] = batched_leg(sf, sf_inputs, torch, args.steps)
+    if not args.no_heads_leg:
+        result["heads_leg"] = heads_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_long_leg:
         result["long_leg"] = long_leg(sf, sf_inputs, torch, args.long_steps)
     result["lds_copy_calibration"] = lds_copy_calibration(sf, torch)
