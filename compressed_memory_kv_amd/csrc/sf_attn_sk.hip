@@ -731,6 +731,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       };
       if (stream == 0) finish(o00, o01);
       else finish(o10, o11);
+      // Marks for the combine, which then merges every piece slot of a unit and needs no
+      // count of its pieces: the column's last piece gives the unit's piece slots past its
+      // own the reference -inf (no partial this launch); a unit written whole gets +inf in
+      // slot 0 (nothing to merge).
+      if (stream == 0 && eg == 0 && tile1 == nt) {
+        const int ke0 = whole ? 0 : k + 1, ke1 = whole ? 1 : S.ppu - 1;
+        const float mark = whole ? INFINITY : -INFINITY;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int row = qrow0 + 32 * qb + el32;
+          if (row >= S.rows) continue;
+          float2* ml = reinterpret_cast<float2*>(S.part_ml) + (size_t)u * S.ppu * kSkRows + (row - qt * kSkRows);
+          for (int ke = ke0; ke < ke1; ++ke) ml[(size_t)ke * kSkRows] = make_float2(mark, 0.0f);
+        }
+      }
     }
     __syncthreads();  // the merge buffer overlays the stages of the next piece
     }
@@ -905,13 +920,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   const SkSession& S = a.s[si];
   const bool has_tail = (S.n_keys & (kSkKeys - 1)) != 0;
   const int qt = u % S.qtiles, h = u / S.qtiles;
-  int pieces = 0;
-  if (S.ntiles > 0) {
-    const int first = S.it_begin + h * S.ntiles;  // the column's first iteration
-    pieces = a.grp_table ? grp_of_tab(a, first + S.ntiles - 1) - grp_of_tab(a, first) + 1
-                         : grp_of_iter<I>(a, first + S.ntiles - 1) - grp_of_iter<I>(a, first) + 1;
-  }
-  if (pieces == 1 && !has_tail) return;  // written whole by one workgroup
+  // Every piece slot but the last: a partial of this launch, or -inf (none); slot 0 holds
+  // +inf when one workgroup wrote the unit whole.  The last slot holds the tail's partial.
+  const int pieces = S.ntiles > 0 ? S.ppu - 1 : 0;
   const int total = pieces + (has_tail ? 1 : 0);
   const int H = a.n_heads;
   constexpr int RSTRIDE = kCombThreads / (D / 4);  // 16 rows between a thread's rows
@@ -940,6 +951,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
         x[j][i] = *reinterpret_cast<const float4*>(S.part_o + (slot * kSkRows + rin) * D + d4);
       }
     }
+    // written whole by one workgroup (the mark is per unit, so uniform over the workgroup)
+    if (k0 == 0 && pieces > 0 && ml[0][0].x == INFINITY) return;
 #pragma unroll
     for (int j = 0; j < kCombBatch; ++j) {
       if (k0 + j >= total) break;
@@ -948,9 +961,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
         const float mn = fmaxf(mx[i], ml[j][i].x);
         const float fo = __builtin_amdgcn_exp2f(mx[i] - mn);  // mx = -inf on the first partial: 0
         const float fn = __builtin_amdgcn_exp2f(ml[j][i].x - mn);
-        l[i] = l[i] * fo + ml[j][i].y * fn;
-        acc[i] = make_float4(acc[i].x * fo + x[j][i].x * fn, acc[i].y * fo + x[j][i].y * fn,
-                             acc[i].z * fo + x[j][i].z * fn, acc[i].w * fo + x[j][i].w * fn);
+        // a slot without a partial (reference -inf) adds nothing, whatever its stale numerators
+        const float4 xn = fn > 0.0f ? make_float4(x[j][i].x * fn, x[j][i].y * fn, x[j][i].z * fn, x[j][i].w * fn)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        l[i] = l[i] * fo + (fn > 0.0f ? ml[j][i].y * fn : 0.0f);
+        acc[i] = make_float4(acc[i].x * fo + xn.x, acc[i].y * fo + xn.y, acc[i].z * fo + xn.z, acc[i].w * fo + xn.w);
         mx[i] = mn;
       }
     }
