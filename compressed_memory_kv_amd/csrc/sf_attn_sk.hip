@@ -890,8 +890,10 @@ static_assert(kCombSplit * kCombRows == kSkRows && kCombPer * kCombThreads == kC
 // Merges the partials of each unit that has more than one, in slot order (pieces, then
 // the tail), and writes the normalised output.  kCombSplit workgroups per unit, each
 // owning kCombRows rows; a thread owns 4 columns of kCombPer rows.  Partials are read
-// kCombBatch at a time, all loads in flight before the first is used.
-template <typename I>
+// kCombBatch at a time, all loads in flight before the first is used.  ONE: a one-session
+// launch, whose session is 0 at compile time (its fields come from fixed argument offsets,
+// with no dependent loads to find it).
+template <bool ONE>
 __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch a, int total_units, int n_wg) {
   // A record written by this launch (one session) and not copied by the attention kernel:
   // the attention read its keys from the source, so the copy into the buffer can wait
@@ -915,8 +917,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_sk_kernel(const SkLaunch
   }
   int ug, part;
   if (!unit_of_wg(a, total_units, kCombSplit, ug, part)) return;
-  int si, u;
-  decode_unit(a, ug, si, u);
+  int si = 0, u = ug;
+  if (!ONE) decode_unit(a, ug, si, u);
   const SkSession& S = a.s[si];
   const bool has_tail = (S.n_keys & (kSkKeys - 1)) != 0;
   const int qt = u % S.qtiles, h = u / S.qtiles;
@@ -1012,8 +1014,8 @@ hipError_t launch_tail_sk(const SkLaunch& a, int total_units, hipStream_t stream
 
 hipError_t launch_combine_sk(const SkLaunch& a, int total_units, hipStream_t stream) {
   const int grid = (a.xcd_map ? 8 * a.xcd_per : total_units) * kCombSplit;
-  if (a.narrow) launch(combine_sk_kernel<unsigned>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
-  else launch(combine_sk_kernel<long long>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
+  if (a.n_sessions == 1) launch(combine_sk_kernel<true>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
+  else launch(combine_sk_kernel<false>, dim3(grid), dim3(kCombThreads), stream, a, total_units, grid);
   return hipGetLastError();
 }
 
