@@ -502,53 +502,49 @@ void attn_bf16_kernel(const AttnLaunch a) {
   }
 }
 
-// Merge key splits: one wave per (row, head); lane covers D/64 output columns.  Every
-// split's partial (reference max, row sum, numerators) is loaded before the first use, so
-// a wave has all its loads in flight at once.
+// Merge key splits: D/4 threads per (row, head), one float4 of the output each, so a
+// workgroup covers 256/(D/4) (row, head) pairs with 16-byte loads.  Every split's partial
+// (reference max, row sum, numerators) is loaded before the first use, so a thread has all
+// its loads in flight at once.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnLaunch a) {
+  constexpr int TPP = D / 4;        // threads per (row, head) pair
+  constexpr int PPW = 256 / TPP;    // pairs per workgroup
   const AttnSession& S = a.s[wg_y()];
   if (S.split <= 1) return;
   const int H = a.n_heads;
-  const int idx = wg_x() * 4 + (tid_x() >> 6);
+  const int idx = wg_x() * PPW + tid_x() / TPP;
   if (idx >= S.rows * H) return;
-  const int lane = tid_x() & 63;
+  const int d4 = (tid_x() % TPP) * 4;
   const size_t slice = (size_t)S.rows * H;  // (row, head) pairs per split
   const int split = S.split;                // <= kMaxSplit
-  constexpr int PER = D / 64;
-  float m[kMaxSplit], l[kMaxSplit], po[kMaxSplit][PER];
+  float m[kMaxSplit], l[kMaxSplit];
+  float4 po[kMaxSplit];
 #pragma unroll
   for (int k = 0; k < kMaxSplit; ++k) {
     m[k] = -INFINITY;
     l[k] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) po[k][j] = 0.0f;
+    po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < split) {
       const float2 ml = *reinterpret_cast<const float2*>(S.part_ml + (k * slice + idx) * 2);
       m[k] = ml.x;
       l[k] = ml.y;
-      const float* p = S.part_o + (k * slice + idx) * D;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) po[k][j] = p[lane + 64 * j];
+      po[k] = *reinterpret_cast<const float4*>(S.part_o + (k * slice + idx) * D + d4);
     }
   }
   float mmax = m[0];
 #pragma unroll
   for (int k = 1; k < kMaxSplit; ++k) mmax = fmaxf(mmax, m[k]);
-  float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lt = 0.0f;
 #pragma unroll
   for (int k = 0; k < kMaxSplit; ++k) {
     const float wgt = __builtin_amdgcn_exp2f(m[k] - mmax);  // 0 for the splits past `split`
     lt += wgt * l[k];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[k][j];
+    acc = make_float4(acc.x + wgt * po[k].x, acc.y + wgt * po[k].y, acc.z + wgt * po[k].z, acc.w + wgt * po[k].w);
   }
   const float inv = 1.0f / lt;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) S.out[(size_t)idx * D + lane + 64 * j] = acc[j] * inv;
+  *reinterpret_cast<float4*>(S.out + (size_t)idx * D + d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -678,11 +674,10 @@ hipError_t launch_combine(const AttnLaunch& a, hipStream_t stream) {
     max_pairs = max_pairs > a.s[i].rows * a.n_heads ? max_pairs : a.s[i].rows * a.n_heads;
   }
   if (!any) return hipSuccess;
-  const dim3 grid((max_pairs + 3) / 4, a.n_sessions);
   if (a.head_dim == 64)
-    launch(combine_kernel<64>, grid, dim3(256), stream, a);
+    launch(combine_kernel<64>, dim3((max_pairs + 15) / 16, a.n_sessions), dim3(256), stream, a);
   else if (a.head_dim == 128)
-    launch(combine_kernel<128>, grid, dim3(256), stream, a);
+    launch(combine_kernel<128>, dim3((max_pairs + 7) / 8, a.n_sessions), dim3(256), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
