@@ -184,6 +184,11 @@ __device__ __forceinline__ int grp_of_tab(const SkLaunch& a, const int i) {
 
 // Session and unit of a unit index counted over the whole launch.
 __device__ __forceinline__ void decode_unit(const SkLaunch& a, int ug, int& si, int& u) {
+  if (a.uni_units > 0) {  // sessions of equal size: no walk (one dependent load per session)
+    si = __builtin_amdgcn_readfirstlane(ug / a.uni_units);
+    u = __builtin_amdgcn_readfirstlane(ug - si * a.uni_units);
+    return;
+  }
   int s = 0, base = 0, acc = 0;
   for (int i = 0; i < a.n_sessions; ++i) {
     if (ug >= acc) {

@@ -807,6 +807,9 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       s.part_o = reinterpret_cast<float*>(base);
       s.part_ml = s.part_o + (size_t)units * s.ppu * sf::kSkRows * 64;
     }
+    a.uni_units = H * a.s[0].qtiles;
+    for (int i = 1; i < cnt; ++i)
+      if (a.s[i].qtiles != a.s[0].qtiles) a.uni_units = 0;
     // Producing XCD of every unit (with whole groups per XCD, group g is on XCD
     // g / grp_per_xcd): the XCD of the group holding its column's first tile; a unit
     // without full tiles goes with the unit before it.

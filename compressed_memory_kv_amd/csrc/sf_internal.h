@@ -164,7 +164,10 @@ struct SkLaunch {
   // The host fills it when n_grp <= kSkGrpTable, N < 2^24 and every slot < 128: the
   // kernel's start-up is bound by the scalar unit, which its CU's 8 waves share.
   int32_t grp_table;
-  int32_t pad_;
+  // H * qtiles when every session of the launch has the same number of query tiles (their
+  // units then split evenly: unit ug is unit ug % uni_units of session ug / uni_units),
+  // else 0 (the sessions are walked).
+  int32_t uni_units;
   SkSession s[kMaxLaunchSessions];
   int32_t grp_first[kSkGrpTable + 1];
 };
