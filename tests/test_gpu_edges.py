@@ -102,3 +102,35 @@ def test_smallest_geometries(wl):
         check_attention(out, ref, wl["dtype"], f"t={t} keys={orc.n_keys()}")
         for bb in range(wl["n_blocks"]):
             check_buffer(sess, orc, bb, f"t={t} b{bb}")
+
+
+@needs_gpu
+def test_whole_units_over_stale_scratch():
+    """Units one workgroup reads whole, over scratch that holds finite stale partials.
+
+    Record of 128 rows (one query tile), 4 heads of 64: at t = 0 each of the 4 columns is
+    two full tiles and one group range, so the stream-K read writes every unit's output
+    itself and marks it; the combine must leave those units alone.  From t = 1 on the
+    columns are cut into several pieces.  The scratch is filled with 1.0f before the first
+    read, so a combine that merged unmarked slots would fold in finite wrong partials."""
+    wl = dict(hw=120, x=8, y=2, w=24, n_heads=4, head_dim=64, n_blocks=1, dtype="bf16", seed=35, v_scale=1.0)
+    g = so.Geometry.from_workload(wl)
+    cfg = sf.make_config(**wl)
+    sess = sf.Session(cfg)
+    torch.cuda.synchronize()
+    kv = sf.sf_kv_bytes(cfg)
+    rest = (sess.mem.numel() - kv) // 4 * 4
+    assert rest > 0
+    sess.mem[kv:kv + rest].view(torch.int32).fill_(0x3F800000)  # 1.0f everywhere in the scratch
+    torch.cuda.synchronize()
+    orc = so.MemoryReplay(g)
+    out = torch.empty(sf_inputs.record_shape(wl), dtype=torch.float32, device="cuda")
+    for t in range(6):
+        q, k, v = sf_inputs.frame_tensors(wl, 0, 0, t, device="cuda")
+        out.fill_(float("nan"))
+        sess.step(0, t, q, k, v, out)
+        orc.step(t, {0: (host(k), host(v))})
+        torch.cuda.synchronize()
+        check_tables(sess, orc, f"t={t}")
+        ma, rel = check_attention(out, orc.attend(0, host(q)), "bf16", f"t={t} keys={orc.n_keys()}")
+        say(f"[whole] t={t} keys={orc.n_keys()} max_abs={ma:.2e} rel_l2={rel:.2e}")
