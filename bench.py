@@ -68,6 +68,8 @@ def parse():
                     help="skip the long-horizon leg (24 heads of 128, 46,688 keys per read)")
     ap.add_argument("--no-batched-leg", action="store_true",
                     help="skip the batched leg (8 sessions at fill levels 0..31, one sf_attend per block)")
+    ap.add_argument("--no-evict-sweep", action="store_true",
+                    help="skip the eviction at 1..112 blocks (fixed cost and streaming rate of the copy)")
     ap.add_argument("--no-heads-leg", action="store_true",
                     help="skip the head-count leg (2/4/8 heads: one GPU's share under head sharding; 20 heads)")
     ap.add_argument("--long-steps", type=int, default=4, help="timed frames of the long-horizon leg")
@@ -305,6 +307,50 @@ def heads_leg(sf, sf_inputs, torch, wl, sink_gap, steps, warmup, heads=(2, 4, 8,
         }
     return {"workload": "served rollout with H heads of 64 (2/4/8: one GPU's share under 8/4/2-way head "
                         "sharding; 20: the model card's width); step = 28 x sf_step", "by_heads": res}
+
+
+def evict_sweep(sf, sf_inputs, torch, frames=12, blocks=(1, 4, 14, 28, 56, 112)):
+    """The all-block eviction at the served shape with 1 to 112 blocks (0.79 to 88 MB moved
+    per launch): its duration against its bytes, fitted as a fixed part plus bytes over a
+    streaming rate, which shows how much of the 28-block eviction is launch and ramp."""
+    wl = sf_inputs.WORKLOADS["rollout"]
+    R, H, D, X = wl["hw"] + wl["x"], wl["n_heads"], wl["head_dim"], wl["x"]
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    _, k, v = sf_inputs.frame_tensors(wl, 0, 0, 0, device=dev)
+    pts = []
+    for nb in blocks:
+        sess = sf.Session(sf.make_config(**dict(wl, n_blocks=nb)), device=dev)
+        h = sess.handle
+        n_t = wl["y"] + 2 + frames
+        for t in range(n_t):
+            if t == wl["y"] + 2:
+                torch.cuda.synchronize()
+                sf.sf_profile_enable(h, True)
+            if t >= 1:
+                sf.sf_evict(h, t, stream)
+            for b in range(nb):
+                sf.sf_write_record(h, b, t, k, v, stream)
+        kt = sf.sf_kernel_times_read(h)
+        sf.sf_profile_enable(h, False)
+        sess.close()
+        us = kt["evict"][0] / max(kt["evict"][1], 1) * 1e3
+        pts.append((nb * 2 * 2 * X * H * D * 2, us, kt["evict"][1]))
+    # least squares: us = a + bytes / rate
+    n = len(pts)
+    mx = sum(b for b, _, _ in pts) / n
+    my = sum(u for _, u, _ in pts) / n
+    sxx = sum((b - mx) ** 2 for b, _, _ in pts)
+    slope = sum((b - mx) * (u - my) for b, u, _ in pts) / sxx
+    fixed = my - slope * mx
+    return {
+        "points": [{"blocks": nb, "bytes": b, "avg_us": round(u, 3), "launches": c,
+                    "gbps": round(b / (u * 1e-6) / 1e9, 1), "frac_hbm": round(b / (u * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+                   for nb, (b, u, c) in zip(blocks, pts)],
+        "fit_fixed_us": round(fixed, 3),
+        "fit_stream_gbps": round(1e-3 / slope, 1) if slope > 0 else None,
+        "fit_stream_frac_hbm": round(1e-3 / slope / PEAK_HBM_GBPS, 4) if slope > 0 else None,
+    }
 
 
 def long_leg(sf, sf_inputs, torch, steps, warmup=1):
@@ -624,6 +670,8 @@ def main():
         result["bias_leg"] = bias_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_batched_leg:
         result["batched_leg"] = batched_leg(sf, sf_inputs, torch, args.steps)
+    if not args.no_evict_sweep:
+        result["evict_sweep"] = evict_sweep(sf, sf_inputs, torch)
     if not args.no_heads_leg:
         result["heads_leg"] = heads_leg(sf, sf_inputs, torch, wl, sink_gap, args.steps, args.warmup)
     if not args.no_long_leg:
