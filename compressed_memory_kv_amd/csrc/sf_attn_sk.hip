@@ -311,11 +311,140 @@ __device__ __forceinline__ int fresh_lane() {
   return v;
 }
 
+// The tail of every unit whose key count is not a multiple of 64: the last keys % 64
+// keys, exact softmax over them (one tile, so the reference is the true max), written as
+// a partial to the unit's last scratch slot.  One workgroup per unit of the launch; wave
+// w holds query rows 32*w .. 32*w+31 of the unit.
+constexpr int kTailWaves = 4;
+// Unit (launch numbering) and part of a tail or combine workgroup: by the unit's producing
+// XCD when the launch maps them (the hardware deals workgroup g to XCD g mod 8), else in
+// order.  False: no unit for this workgroup.
+__device__ __forceinline__ bool unit_of_wg(const SkLaunch& a, int total_units, int split, int& ug, int& part) {
+  if (a.xcd_map) {
+    const int x = (int)(wg_x() & 7u), j = (int)(wg_x() >> 3);
+    ug = a.xcd_first[x] + j / split;
+    part = j % split;
+    return ug < a.xcd_first[x + 1];
+  }
+  ug = (int)wg_x() / split;
+  part = (int)wg_x() % split;
+  return ug < total_units;
+}
+
+// The tail of unit ug (launch numbering) by one 4-wave workgroup, staging in st (STAGE bytes).
+__device__ __forceinline__ void tail_unit(const SkLaunch& a, const int ug, char* st) {
+  int si, u;
+  decode_unit(a, ug, si, u);
+  const SkSession& S = a.s[si];
+  const int nk = S.n_keys & (BN - 1);
+  if (nk == 0) return;  // no tail: uniform over the workgroup
+  const int key0 = S.n_keys - nk;
+  const int H = a.n_heads;
+  const float c = a.scale_log2;
+  const int qt = u % S.qtiles, h = u / S.qtiles;
+  const int tid = tid_x();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int row_stride = H * D;
+  const int row_bytes = 2 * row_stride;
+  int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
+  seg_tables<false>(S, seg_row, seg_key);
+
+  // the 64-row tile of keys key0 .. key0+63 (past the last key: its row again), wave w
+  // moving rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of K and of V (one K chunk per lane for both)
+  {
+    const int drow = lane >> 3;
+    const int kchunk = (lane & 7) ^ (((wave & 1) << 2) | (drow >> 1));
+    const int vchunk = (lane & 7) ^ (2 * (drow & 3));
+    const char* kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
+    const char* vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
+    const char* krec = reinterpret_cast<const char*>(S.rec_k) + 2 * h * D;
+    const char* vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int trow = 8 * wave + 32 * m;
+      const int kappa = min(key0 + trow + drow, S.n_keys - 1);
+      int sg;
+      const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa, sg) * row_bytes);
+      const char* kb = (S.rec_seg >= 0 && sg == kRecSlot) ? krec : kg;
+      const char* vb = (S.rec_seg >= 0 && sg == kRecSlot) ? vrec : vg;
+      __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(st + trow * ROW), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(st + TILE + trow * ROW), 16, 0, 0);
+    }
+  }
+  bf16x8 qop[4];
+  const int qrow = qt * kSkRows + 32 * wave + l32;
+  {
+    const int r = min(qrow, S.rows - 1);
+    const __bf16* qp = reinterpret_cast<const __bf16*>(S.q) + r * row_stride + h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+  }
+  __syncthreads();
+
+  SK_OPERAND_ADDRESSES(0);
+  const f32x16 zero16 = {};
+  f32x16 s[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    bf16x8 kop[4];
+    SK_LOAD_K(kop, st, 32 * hh);
+    SK_QK(s[hh], kop, qop);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (key >= nk) s[hh][r] = -INFINITY;
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) mt = max3(mt, max3(s[0][r], s[0][r + 1], s[1][r]), s[1][r + 1]);
+  const float mref = fmaxf(mt, xor32(mt)) * c;  // key 0 of the tail is real, so this is finite
+  f32x16 oa = zero16, ob = zero16;
+  float l = 0.0f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    bf16x8 vop[4], p[2];
+    SK_LOAD_V(vop, st, 32 * hh);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hh][8 * b + r], c, -mref));
+        p[b][r] = (__bf16)e;
+        l += e;
+      }
+    SK_PV(oa, ob, vop, p);
+  }
+  const float lt = l + xor32(l);
+  if (qrow < S.rows) {
+    const size_t slot = (size_t)u * S.ppu + (S.ppu - 1);
+    const int rin = qrow - qt * kSkRows;
+    float* po = S.part_o + (slot * kSkRows + rin) * D;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      *reinterpret_cast<float4*>(po + 8 * q4 + 4 * g) = make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
+      *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * g) =
+          make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
+    }
+    if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mref, lt);
+  }
+}
+
 template <bool REC, typename I>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sk_kernel(const SkLaunch a) {
   __shared__ __attribute__((aligned(16))) char st_a[STAGE_ALL];  // stage 0 of each stream
   __shared__ __attribute__((aligned(16))) char st_b[STAGE_ALL];  // stage 1 of each stream
   __shared__ int redo[kWaves];
+  // Workgroups past the attention's (SkLaunch::tail_units of them) take the units' tails:
+  // dispatched as attention workgroups finish, they fill the compute units the early
+  // finishers leave.
+  if ((int)wg_x() >= a.n_wg) {
+    tail_unit(a, (int)wg_x() - a.n_wg, st_a);
+    return;
+  }
   const int G = a.n_wg;
   const int w = (G & 7) == 0 ? (int)(wg_x() & 7u) * (G >> 3) + (int)(wg_x() >> 3) : (int)wg_x();
   // group and member of this workgroup
@@ -758,128 +887,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-// The tail of every unit whose key count is not a multiple of 64: the last keys % 64
-// keys, exact softmax over them (one tile, so the reference is the true max), written as
-// a partial to the unit's last scratch slot.  One workgroup per unit of the launch; wave
-// w holds query rows 32*w .. 32*w+31 of the unit.
-constexpr int kTailWaves = 4;
-// Unit (launch numbering) and part of a tail or combine workgroup: by the unit's producing
-// XCD when the launch maps them (the hardware deals workgroup g to XCD g mod 8), else in
-// order.  False: no unit for this workgroup.
-__device__ __forceinline__ bool unit_of_wg(const SkLaunch& a, int total_units, int split, int& ug, int& part) {
-  if (a.xcd_map) {
-    const int x = (int)(wg_x() & 7u), j = (int)(wg_x() >> 3);
-    ug = a.xcd_first[x] + j / split;
-    part = j % split;
-    return ug < a.xcd_first[x + 1];
-  }
-  ug = (int)wg_x() / split;
-  part = (int)wg_x() % split;
-  return ug < total_units;
-}
-
 __global__ __launch_bounds__(kTailWaves * 64) void attn_tail_kernel(const SkLaunch a, int total_units) {
   __shared__ __attribute__((aligned(16))) char st[STAGE];
   int ug, part_unused;
   if (!unit_of_wg(a, total_units, 1, ug, part_unused)) return;
-  int si, u;
-  decode_unit(a, ug, si, u);
-  const SkSession& S = a.s[si];
-  const int nk = S.n_keys & (BN - 1);
-  if (nk == 0) return;  // no tail: uniform over the workgroup
-  const int key0 = S.n_keys - nk;
-  const int H = a.n_heads;
-  const float c = a.scale_log2;
-  const int qt = u % S.qtiles, h = u / S.qtiles;
-  const int tid = tid_x();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-  const int row_stride = H * D;
-  const int row_bytes = 2 * row_stride;
-  int seg_row[SF_MAX_SEGMENTS], seg_key[SF_MAX_SEGMENTS];
-  seg_tables<false>(S, seg_row, seg_key);
-
-  // the 64-row tile of keys key0 .. key0+63 (past the last key: its row again), wave w
-  // moving rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of K and of V (one K chunk per lane for both)
-  {
-    const int drow = lane >> 3;
-    const int kchunk = (lane & 7) ^ (((wave & 1) << 2) | (drow >> 1));
-    const int vchunk = (lane & 7) ^ (2 * (drow & 3));
-    const char* kg = reinterpret_cast<const char*>(S.k) + 2 * h * D;
-    const char* vg = reinterpret_cast<const char*>(S.v) + 2 * h * D;
-    const char* krec = reinterpret_cast<const char*>(S.rec_k) + 2 * h * D;
-    const char* vrec = reinterpret_cast<const char*>(S.rec_v) + 2 * h * D;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int trow = 8 * wave + 32 * m;
-      const int kappa = min(key0 + trow + drow, S.n_keys - 1);
-      int sg;
-      const unsigned rb = (unsigned)(key_row(seg_row, seg_key, kappa, sg) * row_bytes);
-      const char* kb = (S.rec_seg >= 0 && sg == kRecSlot) ? krec : kg;
-      const char* vb = (S.rec_seg >= 0 && sg == kRecSlot) ? vrec : vg;
-      __builtin_amdgcn_global_load_lds(kb + rb + kchunk * 16, (lds_void*)(st + trow * ROW), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + rb + vchunk * 16, (lds_void*)(st + TILE + trow * ROW), 16, 0, 0);
-    }
-  }
-  bf16x8 qop[4];
-  const int qrow = qt * kSkRows + 32 * wave + l32;
-  {
-    const int r = min(qrow, S.rows - 1);
-    const __bf16* qp = reinterpret_cast<const __bf16*>(S.q) + r * row_stride + h * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qop[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-  }
-  __syncthreads();
-
-  SK_OPERAND_ADDRESSES(0);
-  const f32x16 zero16 = {};
-  f32x16 s[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    bf16x8 kop[4];
-    SK_LOAD_K(kop, st, 32 * hh);
-    SK_QK(s[hh], kop, qop);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key >= nk) s[hh][r] = -INFINITY;
-    }
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) mt = max3(mt, max3(s[0][r], s[0][r + 1], s[1][r]), s[1][r + 1]);
-  const float mref = fmaxf(mt, xor32(mt)) * c;  // key 0 of the tail is real, so this is finite
-  f32x16 oa = zero16, ob = zero16;
-  float l = 0.0f;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    bf16x8 vop[4], p[2];
-    SK_LOAD_V(vop, st, 32 * hh);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hh][8 * b + r], c, -mref));
-        p[b][r] = (__bf16)e;
-        l += e;
-      }
-    SK_PV(oa, ob, vop, p);
-  }
-  const float lt = l + xor32(l);
-  if (qrow < S.rows) {
-    const size_t slot = (size_t)u * S.ppu + (S.ppu - 1);
-    const int rin = qrow - qt * kSkRows;
-    float* po = S.part_o + (slot * kSkRows + rin) * D;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      *reinterpret_cast<float4*>(po + 8 * q4 + 4 * g) = make_float4(oa[4 * q4], oa[4 * q4 + 1], oa[4 * q4 + 2], oa[4 * q4 + 3]);
-      *reinterpret_cast<float4*>(po + 32 + 8 * q4 + 4 * g) =
-          make_float4(ob[4 * q4], ob[4 * q4 + 1], ob[4 * q4 + 2], ob[4 * q4 + 3]);
-    }
-    if (g == 0) *reinterpret_cast<float2*>(S.part_ml + (slot * kSkRows + rin) * 2) = make_float2(mref, lt);
-  }
+  tail_unit(a, ug, st);
 }
 
 // Combine tiling: the partials of a unit are its pieces from attn_sk_kernel (slots
@@ -1003,11 +1015,13 @@ size_t sk_scratch_bytes(int64_t rows, int n_heads, int64_t capacity_rows) {
 }
 
 hipError_t launch_attend_sk(const SkLaunch& a, hipStream_t stream) {
+  static_assert(kTailWaves == kWaves, "tail workgroups share the attention launch's shape");
   const bool rec = a.n_sessions == 1 && a.s[0].rec_seg >= 0;
-  if (rec && a.narrow) launch(attn_sk_kernel<true, unsigned>, dim3(a.n_wg), dim3(kThreads), stream, a);
-  else if (rec) launch(attn_sk_kernel<true, long long>, dim3(a.n_wg), dim3(kThreads), stream, a);
-  else if (a.narrow) launch(attn_sk_kernel<false, unsigned>, dim3(a.n_wg), dim3(kThreads), stream, a);
-  else launch(attn_sk_kernel<false, long long>, dim3(a.n_wg), dim3(kThreads), stream, a);
+  const dim3 grid(a.n_wg + a.tail_units);
+  if (rec && a.narrow) launch(attn_sk_kernel<true, unsigned>, grid, dim3(kThreads), stream, a);
+  else if (rec) launch(attn_sk_kernel<true, long long>, grid, dim3(kThreads), stream, a);
+  else if (a.narrow) launch(attn_sk_kernel<false, unsigned>, grid, dim3(kThreads), stream, a);
+  else launch(attn_sk_kernel<false, long long>, grid, dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 

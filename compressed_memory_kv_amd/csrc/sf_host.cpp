@@ -840,6 +840,8 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       const int64_t mean = (units_total + 7) / 8;
       a.xcd_map = 4 * per <= 5 * mean ? 1 : 0;
     }
+    // the tails ride on the attention launch when it runs (see SkLaunch::tail_units)
+    a.tail_units = any_tail && iters > 0 ? (int32_t)units_total : 0;
     if (planning(arena)) continue;
     hipError_t e = hipSuccess;
     if (iters > 0) {
@@ -847,7 +849,7 @@ sf_status enqueue_attend_sk(sf_buffer* const* bufs, int32_t n, int32_t block, co
       e = sf::launch_attend_sk(a, st);
     }
     if (e != hipSuccess) return hip_fail(b0, e, "attention launch");
-    if (any_tail) {
+    if (any_tail && iters == 0) {
       TraceScope ts(b0->trace, SF_K_TAIL, st);
       e = sf::launch_tail_sk(a, (int)units_total, st);
     }

@@ -168,6 +168,9 @@ struct SkLaunch {
   // units then split evenly: unit ug is unit ug % uni_units of session ug / uni_units),
   // else 0 (the sessions are walked).
   int32_t uni_units;
+  // Units whose tails the attention launch takes itself, in workgroups past its n_wg (the
+  // launch's units when any session has a tail and the launch has full tiles), else 0.
+  int32_t tail_units;
   SkSession s[kMaxLaunchSessions];
   int32_t grp_first[kSkGrpTable + 1];
 };
