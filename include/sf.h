@@ -230,8 +230,8 @@ sf_status sf_evict(sf_buffer* buf, int64_t t, void* hip_stream);
  * eviction step of t_cur + 1 must not have run yet (it replaces a summary frame t_cur still
  * sees and may turn Z0): SF_E_STATE otherwise.  bf16 sessions: QK^T and PV on bf16 MFMA with fp32 accumulation, softmax in fp32,
  * probabilities rounded to bf16 before PV.  fp32 sessions: fp32 throughout.  One attention
- * launch per read path and per 16 sessions (plus a tail or combine launch where the keys are
- * split).
+ * launch per read path and per 16 sessions, plus a combine launch where the keys are split
+ * (and, at bf16 head_dim 64, a tail launch for reads shorter than 64 keys).
  * [level] A session under SF_ROPE_LEVEL_* takes q unrotated: it is turned by that session's
  * t_cur (as sf_rope_rows does) into the session's own memory first, one launch per session.
  * [files], [credits] A session with recency_bias = 1 adds its bias (sf_set_recency_bias) to
