@@ -26,10 +26,15 @@
 //     finishes at about the same time.  The part of a unit inside one group's range
 //     is a "piece"; a piece that is the whole unit (and the unit has no tail) writes
 //     the output, otherwise it writes an unnormalised partial (O, reference max, row
-//     sum) to the session's scratch;
-//   attn_tail_kernel: one workgroup per unit with a tail writes the tail's
-//     partial to the unit's last scratch slot;
-//   combine_sk_kernel: merges the partials of every unit that has more than one.
+//     sum) to the session's scratch.  The column's last piece marks the unit's piece
+//     slots past its own as empty (reference -inf), and a whole unit marks slot 0
+//     (+inf), so the combine needs no count of a unit's pieces.  Workgroups past the
+//     persistent ones, one per unit, read the units' tails (a unit's last scratch
+//     slot): the hardware dispatches them as attention workgroups finish;
+//   attn_tail_kernel: the same tail workgroups as a launch of their own, for reads
+//     without a full tile (no attention launch to ride on);
+//   combine_sk_kernel: merges every piece slot and the tail of each unit that is not
+//     marked whole.
 // sf_step launches fold the record write in: the attention kernels read the new
 // record's keys from the caller's K/V (segment slot kRecSlot, after the buffer's
 // keys) and copy the record into the buffer meanwhile with the workgroups past the XCDs'
@@ -168,18 +173,6 @@ __device__ __forceinline__ int grp_of_iter(const SkLaunch& a, const int i) {
   const I X = (I)S.cost_begin + (I)col * m * (I)(S.ntiles + a.piece_cost) +
               m * (I)(a.piece_cost + (local - col * S.ntiles));
   return (int)(((X + 1) * (I)a.n_grp - 1) / (I)a.total_cost);
-}
-
-// Group holding column iteration i from the host's table (SkLaunch::grp_table): the last g
-// whose range starts at or before it.
-__device__ __forceinline__ int grp_of_tab(const SkLaunch& a, const int i) {
-  int lo = 0, hi = a.n_grp - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((a.grp_first[mid] & 0xffffff) <= i) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Session and unit of a unit index counted over the whole launch.
