@@ -81,8 +81,9 @@ struct AttnLaunch {
 // between costs floor(g*T/NG) and floor((g+1)*T/NG) (see SkLaunch::piece_cost), each
 // member of the group the same iterations for its own query tiles.  A unit whose tiles
 // span several groups leaves one partial result per group ("piece") in its session's
-// scratch; keys past the last full tile (the tail) leave one more, from the tail kernel,
-// in the unit's last slot; the combine kernel merges them.
+// scratch; keys past the last full tile (the tail) leave one more, from the unit's tail
+// workgroup (launched past the persistent ones, or on its own when the read has no full
+// tile), in the unit's last slot; the combine kernel merges them.
 constexpr int kSkRows = 128;        // query rows per unit
 constexpr int kSkKeys = 64;         // keys per tile
 constexpr int kSkMinRange = 8;      // fewest tiles of a column a group range starting inside it holds

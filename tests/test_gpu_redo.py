@@ -224,7 +224,7 @@ def test_redo_served_step_reads_record_from_source(scale):
 def test_redo_batched_with_tails():
     """Eight sessions at fill levels 0, 1, 2, 3, 10, 23, 24, 31 (1,104 to 6,528 keys; at 0,
     1, 2 and 10 the keys leave a tail of 16 to 48 past the last full tile, read by the
-    tail kernel) in one batched stream-K launch at a caller scale of 0.25; every session
+    tail workgroups that ride on the attention launch) in one batched stream-K launch at a caller scale of 0.25; every session
     planted in its own visiting order."""
     levels = [0, 1, 2, 3, 10, 23, 24, 31]
     wl = dict(SERVED, seed=11)
